@@ -1,0 +1,547 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes one oracle function against a closed form, brute force over a
+small domain, exact rational arithmetic, an independent library routine (torch
+CPU casts, numpy float64 products, scipy's softmax) or a value printed by a
+specification, chosen so that a plausible mistake (a dropped term, a wrong sign,
+an off-by-one exponent, a transposed operand) fails at least one of them.
+
+Citations name the three sglang pull-request reports the method comes from:
+"Support DeepGEMM for standard MoE dispatch" (PR #33128),
+"Add BF16 support to EP-MoE for DeepGEMM" (PR #17392) and
+"[Feature] Support BF16 and batch-invariant inference with DeepEP v2" (PR #38160).
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from scatter_grouped_gemm_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(bits_u16: np.ndarray) -> np.ndarray:
+    return inputs.from_bf16_bits(bits_u16).float().numpy()
+
+
+def _bf16_of(f32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> bf16 cast (round to nearest even), as bit patterns."""
+    return inputs.bf16_bits(torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(torch.bfloat16))
+
+
+def _e4m3_table() -> np.ndarray:
+    """All 256 e4m3fn codes decoded by torch (NaN codes -> nan)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# compact row bound and layout rule ("Support DeepGEMM for standard MoE
+# dispatch", key source excerpts of _get_compact_all_tokens and
+# _should_use_masked_standard_layout)
+# ---------------------------------------------------------------------------
+
+def _compositions(A, E):
+    for cuts in itertools.combinations(range(A + E - 1), E - 1):
+        prev, parts = -1, []
+        for c in cuts:
+            parts.append(c - prev - 1)
+            prev = c
+        parts.append(A + E - 1 - prev - 1)
+        yield parts
+
+
+def test_compact_bound_is_the_max_over_all_routings(orc):
+    """Brute force: the bound equals the largest padded row count any routing
+    of A assignments over E experts can need (never exceeded, and tight)."""
+    for B in range(1, 5):
+        for E in range(1, 5):
+            for A in range(0, 13):
+                worst = max(sum(-(-c // B) * B for c in parts) for parts in _compositions(A, E))
+                assert orc.compact_rows_bound(A, E, B) == worst, (A, E, B)
+
+
+def test_compact_bound_workload_values(orc):
+    """Hand-evaluated values of the page's formula for the workload shapes."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "compact_bound_workloads.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 5
+    for A, E, B, bound in rows:
+        assert orc.compact_rows_bound(int(A), int(E), int(B)) == int(bound)
+
+
+def test_layout_rule_truth_table(orc):
+    """masked iff there are non-local experts and at most 32 local ones."""
+    assert orc.use_masked_layout(256, 32) is True
+    assert orc.use_masked_layout(256, 33) is False
+    assert orc.use_masked_layout(32, 32) is False
+    assert orc.use_masked_layout(8, 8) is False
+    assert orc.use_masked_layout(64, 1) is True
+    assert orc.use_masked_layout(128, 128) is False
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_spec_points_and_torch(orc):
+    """Decoding against the OFP8 spec's notable values and torch's decoder."""
+    for line in open(os.path.join(GOLDEN, "ofp8_e4m3_points.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        code, val = line.split()
+        got = orc.e4m3_to_f64(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val))
+    table = _e4m3_table()
+    for c in range(256):
+        got = orc.e4m3_to_f64(c)
+        if math.isnan(table[c]):
+            assert math.isnan(got)
+        else:
+            assert got == table[c], c
+
+
+def _rne_e4m3_bruteforce(v: np.ndarray) -> np.ndarray:
+    """Nearest finite e4m3fn code by exhaustive search, ties to the even code,
+    saturating at +-448; the sign of zero follows the input."""
+    table = _e4m3_table()
+    pos = np.array([c for c in range(0, 0x7F)], np.int64)         # 0x00..0x7E, finite >= 0
+    vals = table[pos]
+    a = np.minimum(np.abs(v), 448.0)
+    d = np.abs(a[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among ties prefer the code with an even mantissa (LSB 0)
+    even = (pos[None, :] & 1) == 0
+    pick = np.where((cand & even).any(axis=1), np.argmax(cand & even, axis=1), np.argmax(cand, axis=1))
+    code = pos[pick]
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def test_e4m3_encoder_exhaustive_over_bf16_and_scales(orc):
+    """Every finite bf16 pattern times 2^-e for several e, against exhaustive
+    nearest-code search and against torch's float32 -> float8_e4m3fn cast."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]                 # finite patterns only
+    x = _f32(bits).astype(np.float64)
+    finite = np.isfinite(x)
+    bits, x = bits[finite], x[finite]
+    enc = np.vectorize(orc.e4m3_from_f64, otypes=[np.uint8])
+    for e in (-126, -20, -9, -7, 0, 3, 16, 17, 119):
+        v = np.ldexp(x, -e)
+        keep = np.abs(v) <= 448.0
+        v = v[keep]
+        got = enc(v)
+        assert np.array_equal(got, _rne_e4m3_bruteforce(v)), e
+        v32 = v.astype(np.float32)
+        exact = v32.astype(np.float64) == v
+        ref = torch.from_numpy(v32[exact]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got[exact], ref), e
+
+
+def test_e4m3_encoder_saturates_and_keeps_sign(orc):
+    assert orc.e4m3_from_f64(448.0) == 0x7E
+    assert orc.e4m3_from_f64(463.9) == 0x7E
+    assert orc.e4m3_from_f64(1e9) == 0x7E
+    assert orc.e4m3_from_f64(-1e9) == 0xFE
+    assert orc.e4m3_from_f64(-0.0) == 0x80
+    assert orc.e4m3_from_f64(-2.0 ** -11) == 0x80
+    assert orc.e4m3_from_f64(2.0 ** -10) == 0x00          # tie -> even (0)
+    assert orc.e4m3_from_f64(3 * 2.0 ** -10) == 0x02      # tie 1.5 -> 2
+    assert orc.e4m3_from_f64(float("nan")) == 0x7F
+
+
+def test_bf16_rounding_against_torch_and_exact_rationals(orc):
+    """f64 -> bf16 rounding: float32 inputs against torch's cast; doubles that
+    fall between fp32 values against exact rational nearest-even search."""
+    rng = np.random.default_rng(5)
+    f = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),                     # subnormals
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.3895e38, 1e-45], np.float32),
+    ])
+    enc = np.vectorize(orc.f64_to_bf16, otypes=[np.uint16])
+    assert np.array_equal(enc(f.astype(np.float64)), _bf16_of(f))
+    # doubles with bits below fp32 precision: brute force among neighbours
+    for v in list(rng.standard_normal(300) * 7) + [1 + 2 ** -8 + 2 ** -40, 1 + 2 ** -8 - 2 ** -40]:
+        got = orc.f64_to_bf16(float(v))
+        fv = Fraction(float(v))
+        base = int(_bf16_of(np.array([v], np.float32))[0])
+        best = None
+        for cand in (base - 1, base, base + 1):
+            cv = Fraction(float(_f32(np.array([cand], np.uint16))[0]))
+            key = (abs(cv - fv), cand & 1)
+            if best is None or key < best[0]:
+                best = (key, cand)
+        assert got == best[1], v
+
+
+def _ue8m0_exact(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e, by exact rational search."""
+    if amax == 0:
+        return -126
+    r = Fraction(amax) / 448
+    e = r.numerator.bit_length() - r.denominator.bit_length() - 2
+    while Fraction(2) ** e < r:
+        e += 1
+    return max(-126, min(127, e))
+
+
+def test_ue8m0_exponent_closed_form(orc):
+    """The direct power-of-two scale rule of "Support DeepGEMM for standard MoE
+    dispatch", implementation breakdown item 3, against exact rationals."""
+    bits = np.arange(0, 0x7F80, 7, dtype=np.uint32).astype(np.uint16)     # finite, >= 0
+    vals = _f32(bits).astype(np.float64)
+    for a in list(vals) + [448.0, 448.0 * 2 ** -7, 449.0, 224.0, 2 ** -140]:
+        assert orc.ue8m0_exponent(a) == _ue8m0_exact(a), a
+
+
+# ---------------------------------------------------------------------------
+# quantisation
+# ---------------------------------------------------------------------------
+
+def test_quant_rows_rule_and_torch_cast(orc):
+    """Per row and 128 channels: scale bytes are exact powers of two, the group
+    max lands in (224, 448] unless clamped, and the codes equal torch's cast of
+    x * 2^-e (exact in fp32 for these inputs)."""
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(37, 512, generator=g) * torch.logspace(-3, 3, 37)[:, None]
+    x[3] = 0.0
+    x[4, :128] = 1e-40
+    x[5, 130] = -448.0
+    xb = inputs.bf16_bits(x.to(torch.bfloat16))
+    q, s = orc.quant_rows(xb)
+    xf = _f32(xb).astype(np.float64)
+    e = s.astype(np.int64) - 127
+    assert s.min() >= 1 and s.max() <= 254
+    amax = np.abs(xf.reshape(37, 4, 128)).max(axis=2)
+    ratio = amax / np.ldexp(1.0, e)
+    clamped = e == -126
+    assert np.all(ratio <= 448.0)
+    assert np.all((ratio > 224.0) | clamped)
+    scaled = np.ldexp(xf.reshape(37, 4, 128), -e[:, :, None]).reshape(37, 512).astype(np.float32)
+    ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    assert np.all(s[3] == 1)                                   # all-zero group -> e = -126
+
+
+def test_direct_scale_beats_rounding_the_scale_afterwards(orc):
+    """The page's point: quantising with the power-of-two scale chosen first
+    keeps the e4m3 grid aligned; rounding an amax/448 scale up afterwards
+    without requantising misrepresents values by up to 2x."""
+    g = torch.Generator().manual_seed(2)
+    x = torch.randn(64, 128, generator=g).to(torch.bfloat16)
+    xb = inputs.bf16_bits(x)
+    q, s = orc.quant_rows(xb)
+    xf = x.double().numpy()
+    deq = _e4m3_table()[q] * np.ldexp(1.0, s.astype(np.int64) - 127)
+    err_direct = np.abs(deq - xf).max() / np.abs(xf).max()
+    # after the fact: codes from the exact amax/448 scale, scale then rounded up
+    sc = np.abs(xf).max(axis=1, keepdims=True) / 448.0
+    q2 = torch.from_numpy((xf / sc).astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    sc_up = np.exp2(np.ceil(np.log2(sc)))
+    err_after = np.abs(q2 * sc_up - xf).max() / np.abs(xf).max()
+    assert err_direct < 0.07 and err_after > 0.3
+
+
+def test_quant_weight_blocks_rule(orc):
+    g = torch.Generator().manual_seed(3)
+    w = (torch.randn(2, 256, 384, generator=g) * 0.02).to(torch.bfloat16)
+    w[1, :128, :128] *= 1000
+    wb = inputs.bf16_bits(w)
+    q, s = orc.quant_weight_blocks(wb)
+    wf = w.double().numpy()
+    blocks = np.abs(wf.reshape(2, 2, 128, 3, 128)).max(axis=(2, 4))
+    e = s.astype(np.int64) - 127
+    assert np.all(blocks <= 448.0 * np.ldexp(1.0, e))
+    assert np.all(blocks > 224.0 * np.ldexp(1.0, e))
+    scaled = wf / np.repeat(np.repeat(np.ldexp(1.0, e), 128, axis=1), 128, axis=2)
+    ref = torch.from_numpy(scaled.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def test_route_against_bruteforce_sort_and_scipy_softmax(orc):
+    from scipy.special import softmax
+    rng = np.random.default_rng(7)
+    for T, E, k in [(50, 8, 2), (40, 256, 8), (30, 128, 8), (10, 5, 5)]:
+        L = rng.standard_normal((T, E)).astype(np.float32)
+        L[0, 1] = L[0, 3] = L[0].max() + 1              # explicit tie at the top
+        ids, w = orc.route_topk(L, k)
+        p = softmax(L.astype(np.float64), axis=1)
+        for t in range(T):
+            order = sorted(range(E), key=lambda e: (-L[t, e], e))[:k]
+            assert list(ids[t]) == order
+            sel = p[t, order] / p[t, order].sum()
+            np.testing.assert_allclose(w[t], sel, rtol=2e-7, atol=0)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+        assert ids[0, 0] == 1 and ids[0, 1] == 3
+        if k == E:                                       # full softmax, ordered
+            np.testing.assert_allclose(np.take_along_axis(p, ids, 1), w, rtol=2e-7)
+
+
+# ---------------------------------------------------------------------------
+# scatter
+# ---------------------------------------------------------------------------
+
+def _numpy_compact(ids, expert_start, El, B):
+    """Independent construction: stable argsort of the flat assignments by local
+    expert; non-local assignments dropped."""
+    flat = ids.reshape(-1).astype(np.int64) - expert_start
+    local = (flat >= 0) & (flat < El)
+    a_idx = np.nonzero(local)[0]
+    order = a_idx[np.argsort(flat[a_idx], kind="stable")]
+    counts = np.bincount(flat[a_idx], minlength=El)
+    padded = -(-counts // B) * B
+    start = np.concatenate([[0], np.cumsum(padded)[:-1]])
+    src2dst = np.full(flat.shape, -1, np.int64)
+    seen = np.zeros(El, np.int64)
+    for a in order:
+        e = flat[a]
+        src2dst[a] = start[e] + seen[e]
+        seen[e] += 1
+    return counts, start, src2dst.reshape(ids.shape), padded.sum()
+
+
+@pytest.mark.parametrize("T,H,E,El,start,k,B", [
+    (64, 256, 8, 8, 0, 2, 128), (200, 128, 16, 16, 0, 4, 64), (97, 128, 64, 20, 24, 6, 128),
+    (1, 256, 8, 8, 0, 2, 128), (0, 128, 8, 8, 0, 2, 128)])
+def test_scatter_compact_against_argsort_and_invariants(orc, T, H, E, El, start, k, B):
+    rng = np.random.default_rng(T * 31 + E)
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+    x = inputs.bf16_bits(torch.randn(T, H, generator=torch.Generator().manual_seed(T)).to(torch.bfloat16))
+    R = orc.compact_rows_bound(T * k, El, B)
+    sc = orc.scatter_compact(x, ids, start, El, B, R, fp8=False)
+    counts, st, s2d, used = _numpy_compact(ids, start, El, B)
+    assert np.array_equal(sc["num_valid"], counts)
+    assert np.array_equal(sc["expert_start_loc"], st)
+    assert np.array_equal(sc["src2dst"], s2d)
+    assert used <= R and np.all(st % B == 0)
+    m = sc["m_indices"]
+    for e in range(El):
+        blk = m[st[e]: st[e] + (-(-counts[e] // B) * B)]
+        assert np.all(blk[:counts[e]] == e) and np.all(blk[counts[e]:] == -1)
+    assert np.all(m[used:] == -1)
+    assert (m >= 0).sum() == counts.sum()
+    for t in range(T):
+        for j in range(k):
+            r = sc["src2dst"][t, j]
+            if r >= 0:
+                assert m[r] == ids[t, j] - start
+                assert np.array_equal(sc["x_out"][r], x[t])
+    if counts.sum() > 0:
+        with pytest.raises(ValueError):
+            orc.scatter_compact(x, ids, start, El, B, int(used) - 1, fp8=False)
+
+
+def test_scatter_fp8_rows_equal_quant_of_token(orc):
+    """quant(scatter(x)) == scatter(quant(x)): a scattered FP8 row is the
+    token's own quantisation (the fused quant-and-scatter of "Support DeepGEMM
+    for standard MoE dispatch", implementation breakdown item 3)."""
+    rng = np.random.default_rng(0)
+    T, H, E, k = 33, 384, 8, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = inputs.bf16_bits(torch.randn(T, H, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16))
+    sc = orc.scatter_compact(x, ids, 0, E, 128, orc.compact_rows_bound(T * k, E, 128), fp8=True)
+    q, s = orc.quant_rows(x)
+    for t in range(T):
+        for j in range(k):
+            r = sc["src2dst"][t, j]
+            assert np.array_equal(sc["x_out"][r], q[t]) and np.array_equal(sc["scale_out"][r], s[t])
+
+
+def test_scatter_masked_against_compact(orc):
+    """Masked rows are the compact rows regrouped to e*max_m + rank."""
+    rng = np.random.default_rng(1)
+    T, H, E, El, k = 70, 128, 64, 12, 6
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = inputs.bf16_bits(torch.randn(T, H, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16))
+    mk = orc.scatter_masked(x, ids, 4, El, T, fp8=False)
+    cp = orc.scatter_compact(x, ids, 4, El, 128, orc.compact_rows_bound(T * k, El, 128), fp8=False)
+    assert np.array_equal(mk["masked_m"], cp["num_valid"])
+    local = cp["src2dst"] >= 0
+    assert np.array_equal(mk["src2dst"] >= 0, local)
+    e = (mk["src2dst"] // T)[local]
+    rank_m = (mk["src2dst"] % T)[local]
+    rank_c = cp["src2dst"][local] - cp["expert_start_loc"][e]
+    assert np.array_equal(rank_m, rank_c)
+    assert np.array_equal(e, (ids - 4)[local])
+    with pytest.raises(ValueError):
+        orc.scatter_masked(x, ids, 4, El, int(mk["masked_m"].max()) - 1, fp8=False)
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM, SiLU-and-mul, combine
+# ---------------------------------------------------------------------------
+
+def _rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def test_gemm_bf16_against_numpy_and_exact_on_integers(orc):
+    g = torch.Generator().manual_seed(4)
+    M, N, K, G = 40, 96, 320, 3
+    A = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    B = (torch.randn(G, N, K, generator=g) * 0.05).to(torch.bfloat16)
+    rg = np.array([i % G if i % 7 else -1 for i in range(M)], np.int32)
+    C = orc.gemm_bf16_rows(inputs.bf16_bits(A), inputs.bf16_bits(B), rg)
+    Cf = _f32(C).astype(np.float64)
+    An, Bn = A.double().numpy(), B.double().numpy()
+    for r in range(M):
+        if rg[r] < 0:
+            assert np.all(C[r] == 0)
+            continue
+        ref = Bn[rg[r]] @ An[r]
+        np.testing.assert_allclose(Cf[r], ref, rtol=1e-2, atol=1e-2 * np.abs(ref).max())
+    # integer-valued operands: every partial sum is exact, so the result is the
+    # exact product rounded once to bf16 (torch's cast of the exact fp32 value)
+    Ai = torch.randint(-4, 5, (M, K), generator=g).to(torch.bfloat16)
+    Bi = torch.randint(-3, 4, (G, N, K), generator=g).to(torch.bfloat16)
+    Ci = orc.gemm_bf16_rows(inputs.bf16_bits(Ai), inputs.bf16_bits(Bi), rg)
+    for r in np.nonzero(rg >= 0)[0]:
+        exact = (Bi[rg[r]].double().numpy() @ Ai[r].double().numpy()).astype(np.float32)
+        assert np.array_equal(Ci[r], _bf16_of(exact))
+
+
+def test_gemm_fp8_against_numpy_dequantised(orc):
+    g = torch.Generator().manual_seed(5)
+    M, N, K, G = 24, 256, 384, 2
+    A = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    W = (torch.randn(G, N, K, generator=g) * 0.02).to(torch.bfloat16)
+    aq, as_ = orc.quant_rows(inputs.bf16_bits(A))
+    wq, ws = orc.quant_weight_blocks(inputs.bf16_bits(W))
+    rg = (np.arange(M) % G).astype(np.int32)
+    C = orc.gemm_fp8_rows(aq, as_, wq, ws, rg)
+    tab = _e4m3_table()
+    Ad = tab[aq] * np.repeat(np.ldexp(1.0, as_.astype(np.int64) - 127), 128, axis=1)
+    Wd = tab[wq] * np.repeat(np.repeat(np.ldexp(1.0, ws.astype(np.int64) - 127), 128, 1), 128, 2)
+    ref = np.stack([Wd[rg[r]] @ Ad[r] for r in range(M)])
+    assert _rel_fro(_f32(C), ref) < 4e-3
+    # integer codes with unit scales: exact sums; a transposed or mis-scaled
+    # operand would not reproduce them
+    qa = torch.randint(-6, 7, (M, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    qw = torch.randint(-6, 7, (G, N, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sa = np.full((M, K // 128), 127, np.uint8)
+    sa[:, 1] = 128                                          # second k block scaled by 2
+    sw = np.full((G, N // 128, K // 128), 127, np.uint8)
+    sw[1, 1, 2] = 125                                       # one weight block scaled by 1/4
+    Ci = orc.gemm_fp8_rows(qa, sa, qw, sw, rg)
+    Ad = tab[qa] * np.repeat(np.ldexp(1.0, sa.astype(np.int64) - 127), 128, axis=1)
+    Wd = tab[qw] * np.repeat(np.repeat(np.ldexp(1.0, sw.astype(np.int64) - 127), 128, 1), 128, 2)
+    for r in range(M):
+        exact = (Wd[rg[r]] @ Ad[r]).astype(np.float32)
+        assert np.array_equal(Ci[r], _bf16_of(exact))
+
+
+def test_silu_and_mul_reference_and_special_values(orc):
+    g = torch.Generator().manual_seed(6)
+    M, I = 16, 256
+    gu = (torch.randn(M, 2 * I, generator=g) * 4).to(torch.bfloat16)
+    gu[0, :I] = 0.0
+    gu[1, :I] = 60.0
+    gu[2, :I] = -60.0
+    rg = np.arange(M, dtype=np.int32)
+    rg[5] = -1
+    out = orc.silu_and_mul(inputs.bf16_bits(gu), rg)
+    gd, ud = gu[:, :I].double().numpy(), gu[:, I:].double().numpy()
+    ref = gd / (1 + np.exp(-gd)) * ud
+    of = _f32(out).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    ok = np.abs(of - ref) <= 0.5 * ulp + 1e-300
+    ok[5] = True
+    assert ok.all()
+    assert np.all(of[0] == 0) and np.all(out[5] == 0)
+    assert np.array_equal(out[1], inputs.bf16_bits(gu[1, I:] * 60.0))   # silu(60) == 60 in fp64->bf16
+
+
+def test_combine_bruteforce_and_identity(orc):
+    g = torch.Generator().manual_seed(8)
+    T, k, H, R = 20, 4, 64, 90
+    Y = torch.randn(R, H, generator=g).to(torch.bfloat16)
+    rng = np.random.default_rng(3)
+    s2d = np.stack([rng.permutation(R)[:k] for _ in range(T)]).astype(np.int32)
+    s2d[3, 1] = -1
+    s2d[4, :] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    out = orc.combine(inputs.bf16_bits(Y), s2d, w)
+    Yf = Y.float().numpy()
+    ref = np.zeros((T, H), np.float32)
+    for t in range(T):
+        for j in range(k):                        # float32 sequential, IEEE single ops
+            if s2d[t, j] >= 0:
+                ref[t] = ref[t] + np.float32(w[t, j]) * Yf[s2d[t, j]]
+    assert np.array_equal(out, _bf16_of(ref))
+    assert np.all(_f32(out[4]) == 0)
+    one = orc.combine(inputs.bf16_bits(Y), s2d[:, :1].copy(), np.ones((T, 1), np.float32))
+    for t in range(T):
+        if s2d[t, 0] >= 0:
+            assert np.array_equal(one[t], inputs.bf16_bits(Y)[s2d[t, 0]])
+
+
+# ---------------------------------------------------------------------------
+# layer composition
+# ---------------------------------------------------------------------------
+
+def _weights_np(w13, w2, fp8, orc):
+    if not fp8:
+        return dict(w13=inputs.bf16_bits(w13), w2=inputs.bf16_bits(w2))
+    a, b = orc.quant_weight_blocks(inputs.bf16_bits(w13))
+    c, d = orc.quant_weight_blocks(inputs.bf16_bits(w2))
+    return dict(w13q=a, w13s=b, w2q=c, w2s=d)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_dense_equals_compact_equals_masked(orc, fp8):
+    """The layout is only a permutation: dense, compact and masked chains give
+    the same bits (masked and compact end to end, as in the test intent of
+    "Support DeepGEMM for standard MoE dispatch", implementation breakdown 5)."""
+    T, H, I, E, El, k, start = 40, 256, 256, 16, 6, 4, 5
+    x, L, w13, w2 = inputs.small_case(11, T, H, I, E, k, El=El)
+    W = _weights_np(w13, w2, fp8, orc)
+    xb, Ln = inputs.bf16_bits(x), L.numpy()
+    cp = orc.moe_layer(xb, Ln, k, expert_start=start, num_local_experts=El, layout="compact",
+                       fp8=fp8, **W)
+    mk = orc.moe_layer(xb, Ln, k, expert_start=start, num_local_experts=El, layout="masked",
+                       fp8=fp8, max_m=T, **W)
+    dn = orc.moe_dense(xb, cp["topk_ids"], cp["topk_weights"], start, El, fp8, **W)
+    assert np.array_equal(cp["out"], mk["out"])
+    assert np.array_equal(cp["out"], dn)
+    nonlocal_tok = np.all((cp["topk_ids"] < start) | (cp["topk_ids"] >= start + El), axis=1)
+    assert np.all(_f32(dn[nonlocal_tok]) == 0)
+    # per-token independence: a prefix of the batch gives the same rows
+    dn7 = orc.moe_dense(xb[:7], cp["topk_ids"][:7], cp["topk_weights"][:7], start, El, fp8, **W)
+    assert np.array_equal(dn7, dn[:7])
+
+
+def test_bf16_layer_close_to_fp64_unrounded_chain(orc):
+    """Sanity bound on intermediate bf16 rounding: the oracle's layer against a
+    float64 chain with no intermediate rounding."""
+    T, H, I, E, k = 48, 256, 512, 8, 2
+    x, L, w13, w2 = inputs.small_case(12, T, H, I, E, k)
+    res = orc.moe_layer(inputs.bf16_bits(x), L.numpy(), k, expert_start=0, num_local_experts=E,
+                        layout="compact", fp8=False, w13=inputs.bf16_bits(w13), w2=inputs.bf16_bits(w2))
+    from scipy.special import softmax
+    xd, w13d, w2d = x.double().numpy(), w13.double().numpy(), w2.double().numpy()
+    p = softmax(L.double().numpy(), axis=1)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        top = sorted(range(E), key=lambda e: (-L[t, e].item(), e))[:k]
+        ws = p[t, top] / p[t, top].sum()
+        for e, wj in zip(top, ws):
+            h = w13d[e] @ xd[t]
+            a = h[:I] / (1 + np.exp(-h[:I])) * h[I:]
+            ref[t] += wj * (w2d[e] @ a)
+    assert _rel_fro(_f32(res["out"]), ref) < 5e-3
