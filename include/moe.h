@@ -1,0 +1,254 @@
+/*
+ * libmoe -- routed-token scatter -> grouped GEMM MoE expert path for MI355X
+ * (gfx950), as a C ABI.
+ *
+ * Sources ("the pages"): three sglang pull-request reports --
+ *   [P1] "Support DeepGEMM for standard MoE dispatch" (PR #33128)
+ *   [P2] "Add BF16 support to EP-MoE for DeepGEMM" (PR #17392)
+ *   [P3] "[Feature] Support BF16 and batch-invariant inference with DeepEP v2"
+ *        (PR #38160)
+ *
+ * General contract
+ *   - Every pointer named "device" is a device pointer on the current HIP
+ *     device; the caller owns all memory.  The library never allocates: scratch
+ *     comes in through ws/ws_bytes (size from moe_scatter_ws_bytes).
+ *   - Every compute call validates its arguments on the host first and returns
+ *     a status without launching anything when they are wrong; otherwise it
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = default stream)
+ *     and returns without synchronising.  No call reads device data back to the
+ *     host, so all sizes are fixed by the host arguments (static shapes, P1
+ *     implementation breakdown item 2: buffers usable under graph capture).
+ *   - Buffers may be uninitialised on entry (P1 implementation breakdown item 4):
+ *     every valid row is written before it is read.  Rows marked -1 in
+ *     m_indices, and masked rows at or past masked_m, hold unspecified values in
+ *     every output.
+ *   - Sizes and byte offsets are 64-bit inside the library.
+ *   - bf16 tensors are raw 16-bit patterns; e4m3 is OCP float8 e4m3fn (bias 7,
+ *     max 448); a UE8M0 scale byte s stands for 2^(s-127).
+ *   - Activation scale layout ("K-block major"): compact rows use
+ *     scale[b * M + r] for row r of M and 128-channel block b; masked rows use
+ *     scale[(g * (K/128) + b) * max_m + r] for row r of group g.  Weight scales
+ *     are [G][N/128][K/128].
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL 1          /* null pointer, negative or inconsistent size */
+#define MOE_EUNSUPPORTED 2    /* dtype / alignment the kernels do not cover */
+#define MOE_ECAPACITY 3       /* a static buffer is below the required bound */
+#define MOE_EDEVICE 4         /* a HIP launch or copy failed */
+
+/* element types */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_FP8_E4M3_UE8M0 1
+
+/* device error word bits (see moe_get_device_error) */
+#define MOE_DEVERR_MASKED_OVERFLOW 1  /* an expert received more than max_m rows */
+
+/* ---------------------------------------------------------------------------
+ * Host helpers (no device work)
+ * ------------------------------------------------------------------------- */
+
+/* Static row bound of the compact layout, P1 key source excerpt of
+ * _get_compact_all_tokens: block_e * (min(A, E) + (A - min(A, E)) / block_e)
+ * with A = num_assignments and E = num_local_experts.  No routing of A
+ * assignments over E experts can need more rows when every non-empty expert is
+ * padded to a multiple of block_e.  Returns -1 for negative or zero sizes. */
+int64_t moe_compact_rows_bound(int64_t num_assignments, int32_t num_local_experts,
+                               int32_t block_e);
+
+/* Layout rule, P1 key source excerpt of _should_use_masked_standard_layout:
+ * 1 (masked) when num_experts > num_local_experts and num_local_experts <= 32,
+ * else 0 (compact). */
+int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_experts);
+
+/* Scratch bytes moe_scatter_compact / moe_scatter_masked need for T tokens,
+ * top-k and num_local_experts local experts. */
+size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts);
+
+/* Static text for a status code. */
+const char* moe_status_str(int32_t status);
+
+/* Copies the device error word kept at the start of a scatter workspace to
+ * *host_err after waiting for `stream`; 0 means no data-dependent error was
+ * seen by the last scatter call that used this workspace.  Synchronises. */
+int32_t moe_get_device_error(const void* ws, int32_t* host_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Routing
+ * ------------------------------------------------------------------------- */
+
+/* Top-k routing: softmax over E experts, the k most probable kept and their
+ * probabilities renormalised to sum to 1 (the router output the pages feed
+ * into dispatch as topk_output; P3 related-PR note keeps the router in fp32).
+ *   logits        device fp32 [T][E]
+ *   topk_ids      device int32 [T][k], out: slot j holds the j-th most
+ *                 probable expert; equal logits go to the lower index.
+ *   topk_weights  device fp32 [T][k], out.
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), T >= 0. */
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Scatter into the expert layouts
+ * ------------------------------------------------------------------------- */
+
+/* Compact ("contiguous") layout, P1 implementation breakdown items 2-4 and the
+ * key source excerpt of _fwd_kernel_ep_scatter_1.  Assignment (t, j) is local
+ * when e = topk_ids[t][j] - expert_start lies in [0, num_local_experts)
+ * (P3 implementation breakdown item 1).  Local rows are grouped by expert e in
+ * increasing e; inside an expert they follow increasing (t, j).  Each
+ * non-empty expert is padded to a multiple of block_e rows.
+ *   x                 device bf16 [T][H]
+ *   rows_capacity     rows of every per-row output; must be at least
+ *                     moe_compact_rows_bound(T*k, num_local_experts, block_e)
+ *                     (else MOE_ECAPACITY)
+ *   out_dtype         MOE_DTYPE_BF16: x_out bf16 [rows_capacity][H] copies;
+ *                     MOE_DTYPE_FP8_E4M3_UE8M0: x_out e4m3 [rows_capacity][H]
+ *                     with scale_out [H/128][rows_capacity] (the token's own
+ *                     per-128-channel UE8M0 quantisation, see
+ *                     moe_quant_fp8_ue8m0)
+ *   m_indices         device int32 [rows_capacity], out: e on valid rows, -1 on
+ *                     padding rows and on every row past the last expert block
+ *   expert_start_loc  device int32 [num_local_experts], out: first row of e
+ *   num_valid         device int32 [num_local_experts], out: rows of e
+ *   src2dst           device int32 [T][k], out: row of (t, j), -1 if not local
+ *   ws, ws_bytes      scratch, at least moe_scatter_ws_bytes(T, k, El)
+ * Limits: H % 128 == 0, block_e a positive multiple of 128 (the grouped GEMM
+ * tiles never straddle experts), 1 <= num_local_experts <= 1024,
+ * rows_capacity < 2^31. */
+int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                            int32_t k, int32_t expert_start, int32_t num_local_experts,
+                            int32_t block_e, int64_t rows_capacity, int32_t out_dtype,
+                            void* x_out, uint8_t* scale_out, int32_t* m_indices,
+                            int32_t* expert_start_loc, int32_t* num_valid, int32_t* src2dst,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Masked layout, P1 implementation breakdown item 2 (masked branch) and P2 key
+ * source excerpt of _BF16GroupedMaskedWarmupExecutor: expert e's rows are
+ * x_out[e][0 .. masked_m[e]) in increasing (t, j); src2dst holds the flat row
+ * e*max_m + rank so moe_combine serves both layouts.
+ *   x_out      [num_local_experts][max_m][H] bf16 or e4m3
+ *   scale_out  FP8 only: [num_local_experts][H/128][max_m]
+ *   masked_m   device int32 [num_local_experts], out
+ * max_m must be >= T (a token contributes at most one row per expert when its
+ * k ids are distinct), else MOE_ECAPACITY.  Repeated ids inside one token that
+ * push an expert past max_m set MOE_DEVERR_MASKED_OVERFLOW in the device error
+ * word; the overflowing rows are dropped (src2dst = -1) and masked_m is
+ * clamped to max_m. */
+int32_t moe_scatter_masked(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                           int32_t k, int32_t expert_start, int32_t num_local_experts,
+                           int32_t max_m, int32_t out_dtype, void* x_out, uint8_t* scale_out,
+                           int32_t* masked_m, int32_t* src2dst, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Quantisation
+ * ------------------------------------------------------------------------- */
+
+/* Per-token, per-128-channel FP8 e4m3 with UE8M0 scales computed directly
+ * (P1 implementation breakdown item 3; P3 key source excerpt of the dispatch
+ * path calling per-token-group quantisation with ue8m0): for each group the
+ * exponent e is the smallest integer in [-126, 127] with amax <= 448 * 2^e, then
+ * each value is x * 2^-e rounded to nearest-even e4m3.
+ *   x          device bf16, row r at x + r*ld_x (elements)
+ *   m_indices  optional device int32 [M]; rows with a negative entry are skipped
+ *   q          device e4m3 [M][K]
+ *   scale      device u8 [K/128][M]
+ * Limits: K % 128 == 0, ld_x >= K. */
+int32_t moe_quant_fp8_ue8m0(const void* x, int64_t M, int32_t K, int64_t ld_x,
+                            const int32_t* m_indices, uint8_t* q, uint8_t* scale,
+                            void* stream);
+
+/* Expert weights to 128x128 block-scaled e4m3 with UE8M0 block scales (the same
+ * rule over each block; P1 implementation breakdown item 1 expresses both w13
+ * and w2 with power-of-two block scales).
+ *   w      device bf16 [G][N][K];  q  device e4m3 [G][N][K]
+ *   scale  device u8 [G][N/128][K/128]
+ * Limits: N % 128 == 0, K % 128 == 0. */
+int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t N, int32_t K,
+                                   uint8_t* q, uint8_t* scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped GEMMs ("NT": C = A . B[g]^T), fp32 accumulation, bf16 output
+ * ------------------------------------------------------------------------- */
+
+/* Contiguous layout, P2 key source excerpts of _BF16GroupedContWarmupExecutor
+ * and _run_bf16_contiguous_gemm: C[r, :] = A[r, :] . B[m_indices[r]]^T.
+ *   dtype     MOE_DTYPE_BF16 (A bf16 [M][K], B bf16 [G][N][K]; scales NULL) or
+ *             MOE_DTYPE_FP8_E4M3_UE8M0 (A e4m3 [M][K] with A_scale [K/128][M],
+ *             B e4m3 [G][N][K] with B_scale [G][N/128][K/128])
+ *   C         device bf16 [M][N]; rows with m_indices[r] < 0 are not written
+ *   m_indices device int32 [M]; layout contract: every aligned 128-row block
+ *             holds one expert id on its valid rows, valid rows come first
+ *             (what moe_scatter_compact produces with block_e % 128 == 0)
+ * Limits: N % 128 == 0, K % 128 == 0, 0 <= m_indices < G.
+ * FP8 without scales -> MOE_EUNSUPPORTED (the dtype follows the weights and a
+ * contradiction is an error, P3 implementation breakdown item 2). */
+int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale,
+                            const void* B, const uint8_t* B_scale, void* C,
+                            const int32_t* m_indices, int64_t M, int32_t N, int32_t K,
+                            int32_t G, void* stream);
+
+/* Masked layout, P2 key source excerpt of _BF16GroupedMaskedWarmupExecutor:
+ * C[g, r, :] = A[g, r, :] . B[g]^T for r < masked_m[g].
+ *   A [G][max_m][K], C [G][max_m][N]; FP8 A_scale [G][K/128][max_m].
+ *   expected_m  a hint of typical masked_m (sizes tiles); it never changes a
+ *               result.  0 = no hint.
+ * Limits as grouped_gemm_contig. */
+int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
+                            const void* B, const uint8_t* B_scale, void* C,
+                            const int32_t* masked_m, int32_t expected_m, int32_t max_m,
+                            int32_t N, int32_t K, int32_t G, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Activation and combine
+ * ------------------------------------------------------------------------- */
+
+/* SiLU-and-mul, P2 key source excerpt of _run_bf16_contiguous_gemm (the w13
+ * output [M][2I] is halved): out[r][i] = silu(gateup[r][i]) * gateup[r][I+i],
+ * computed in fp32 and rounded to bf16; for FP8 output that bf16 row is then
+ * quantised as moe_quant_fp8_ue8m0 does.
+ *   Row selection: m_indices (compact; rows with -1 skipped) or masked_m with
+ *   max_m (masked; M = G*max_m, rows r % max_m >= masked_m[r / max_m] skipped);
+ *   both NULL = every row.
+ *   out_scale  FP8 only: compact [I/128][M], masked [G][I/128][max_m].
+ * Limits: I % 128 == 0. */
+int32_t silu_and_mul(const void* gateup, int64_t M, int32_t I, const int32_t* m_indices,
+                     const int32_t* masked_m, int32_t max_m, int32_t out_dtype, void* out,
+                     uint8_t* out_scale, void* stream);
+
+/* Weighted combine back to token order (P1 risks item 2: the post-permute
+ * reads src2dst; P3 review notes: combine follows per-slot pointers):
+ * out[t][h] = sum over j = 0..k-1 with src2dst[t][j] >= 0 of
+ * topk_weights[t][j] * Y[src2dst[t][j]][h], each product and partial sum
+ * rounded to fp32 in slot order, then one rounding to bf16; tokens with no
+ * local slot get 0.
+ *   Y bf16 [num_rows][H]; out bf16 [T][H].  A src2dst entry >= num_rows is
+ *   treated as -1 (never read).  Limits: H % 8 == 0, 1 <= k <= 32. */
+int32_t moe_combine(const void* Y, int64_t num_rows, const int32_t* src2dst,
+                    const float* topk_weights, int32_t T, int32_t k, int32_t H, void* out,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tuning
+ * ------------------------------------------------------------------------- */
+
+/* Number of M tiles that sweep the N tiles together in the grouped GEMMs' tile
+ * order (default 8).  Changes only the order tiles run in, never a result.
+ * Process-wide.  Returns MOE_EINVAL for values < 1. */
+int32_t moe_gemm_set_group_m(int32_t group_m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -151,12 +151,15 @@ def quant_weight_blocks(w: np.ndarray):
 
 
 def scatter_compact(x, topk_ids, expert_start, num_local_experts, block_e,
-                    rows_capacity, fp8: bool):
+                    rows_capacity, fp8: bool, rows: bool = True):
+    """rows=False computes only the indices (no scattered rows)."""
     x = _c(x, np.uint16)
     ids = _c(topk_ids, np.int32)
     T, H = x.shape
     k = ids.shape[1]
-    if fp8:
+    if not rows:
+        x_out = s_out = None
+    elif fp8:
         x_out = np.zeros((rows_capacity, H), np.uint8)
         s_out = np.zeros((rows_capacity, H // 128), np.uint8)
     else:
@@ -176,17 +179,20 @@ def scatter_compact(x, topk_ids, expert_start, num_local_experts, block_e,
                 expert_start_loc=start, num_valid=nvalid, src2dst=src2dst)
 
 
-def scatter_masked(x, topk_ids, expert_start, num_local_experts, max_m, fp8: bool):
+def scatter_masked(x, topk_ids, expert_start, num_local_experts, max_m, fp8: bool,
+                   rows: bool = True):
     x = _c(x, np.uint16)
     ids = _c(topk_ids, np.int32)
     T, H = x.shape
     k = ids.shape[1]
-    rows = num_local_experts * max_m
-    if fp8:
-        x_out = np.zeros((rows, H), np.uint8)
-        s_out = np.zeros((rows, H // 128), np.uint8)
+    nrows = num_local_experts * max_m
+    if not rows:
+        x_out = s_out = None
+    elif fp8:
+        x_out = np.zeros((nrows, H), np.uint8)
+        s_out = np.zeros((nrows, H // 128), np.uint8)
     else:
-        x_out = np.zeros((rows, H), np.uint16)
+        x_out = np.zeros((nrows, H), np.uint16)
         s_out = None
     masked_m = np.empty(num_local_experts, np.int32)
     src2dst = np.empty((T, k), np.int32)

@@ -234,6 +234,7 @@ static int32_t local_of(int32_t id, int32_t expert_start, int32_t num_local) {
 
 static void put_row(const uint16_t* xt, int32_t H, int32_t fp8, void* x_out,
                     uint8_t* scale_out, int64_t row) {
+  if (!x_out) return; /* index-only call */
   if (fp8) {
     quant_row(xt, H, (uint8_t*)x_out + row * H, scale_out + row * (H / 128));
   } else {
@@ -340,6 +341,16 @@ int32_t orc_scatter_masked(const uint16_t* x, int32_t T, int32_t H,
 /* grouped GEMM, SiLU-and-mul, combine                                       */
 /* ------------------------------------------------------------------------ */
 
+/* e4m3 code -> float, filled once from orc_e4m3_to_f64 (every code is exact in
+ * fp32); only a faster way to read the same values. */
+static float g_e4m3[256];
+static int g_e4m3_ready = 0;
+static void e4m3_table_init(void) {
+  if (g_e4m3_ready) return;
+  for (int c = 0; c < 256; ++c) g_e4m3[c] = (float)orc_e4m3_to_f64((uint8_t)c);
+  g_e4m3_ready = 1;
+}
+
 /* One output row of the NT product: c[n] = sum_k a[k] * b[n][k]. */
 static void gemm_row_bf16(const uint16_t* a, const uint16_t* b, int32_t N, int32_t K, uint16_t* c) {
   for (int32_t n = 0; n < N; ++n) {
@@ -362,7 +373,7 @@ static void gemm_row_fp8(const uint8_t* a, const uint8_t* as, const uint8_t* b,
     for (int32_t blk = 0; blk < kb; ++blk) {
       float part = 0.0f;
       for (int32_t kk = blk * 128; kk < blk * 128 + 128; ++kk)
-        part += (float)orc_e4m3_to_f64(a[kk]) * (float)orc_e4m3_to_f64(bn[kk]);
+        part += g_e4m3[a[kk]] * g_e4m3[bn[kk]];
       int32_t ea = (int32_t)as[blk] - 127;
       int32_t eb = (int32_t)bs[(int64_t)(n / 128) * kb + blk] - 127;
       acc += (float)ldexp((double)part, ea + eb);
@@ -385,6 +396,7 @@ void orc_gemm_fp8_rows(const uint8_t* A, const uint8_t* A_scale_rowmajor, int64_
                        const uint8_t* B, const uint8_t* B_scale,
                        int32_t N, int32_t K, const int32_t* row_group, uint16_t* C) {
   int32_t kb = K / 128;
+  e4m3_table_init();
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < M; ++r) {
     int32_t g = row_group[r];
@@ -445,6 +457,7 @@ void orc_moe_dense(const uint16_t* x, int32_t T, int32_t H, int32_t I,
                    const uint8_t* w2q, const uint8_t* w2s,
                    uint16_t* out) {
   int32_t N13 = 2 * I;
+  e4m3_table_init();
 #pragma omp parallel
   {
     uint16_t* h1 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N13);

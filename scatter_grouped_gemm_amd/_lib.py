@@ -1,0 +1,195 @@
+"""ctypes binding of libmoe (include/moe.h), one Python function per C entry point.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their data pointers and torch's current HIP stream are handed
+to the C call.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  If libmoe.so has not been built, loading fails
+with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EDEVICE = 0, 1, 2, 3, 4
+MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0 = 0, 1
+MOE_DEVERR_MASKED_OVERFLOW = 1
+
+# name -> (restype, argtypes); the exported symbols of include/moe.h
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "moe_compact_rows_bound": (_I64, [_I64, _I32, _I32]),
+    "moe_use_masked_layout": (_I32, [_I32, _I32]),
+    "moe_scatter_ws_bytes": (_SZ, [_I32, _I32, _I32]),
+    "moe_status_str": (ctypes.c_char_p, [_I32]),
+    "moe_get_device_error": (_I32, [_P, _P, _P]),
+    "moe_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_scatter_compact": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I32,
+                                   _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_scatter_masked": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_quant_fp8_ue8m0": (_I32, [_P, _I64, _I32, _I64, _P, _P, _P, _P]),
+    "moe_quant_weight_fp8_ue8m0": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "grouped_gemm_contig": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "grouped_gemm_masked": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "silu_and_mul": (_I32, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "moe_combine": (_I32, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_gemm_set_group_m": (_I32, [_I32]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run `python -m scatter_grouped_gemm_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous"
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(fp8: bool) -> int:
+    return MOE_DTYPE_FP8_E4M3_UE8M0 if fp8 else MOE_DTYPE_BF16
+
+
+# --- host helpers ---------------------------------------------------------------
+
+def moe_compact_rows_bound(num_assignments: int, num_local_experts: int, block_e: int = 128) -> int:
+    return int(lib().moe_compact_rows_bound(num_assignments, num_local_experts, block_e))
+
+
+def moe_use_masked_layout(num_experts: int, num_local_experts: int) -> bool:
+    return bool(lib().moe_use_masked_layout(num_experts, num_local_experts))
+
+
+def moe_scatter_ws_bytes(T: int, k: int, num_local_experts: int) -> int:
+    return int(lib().moe_scatter_ws_bytes(T, k, num_local_experts))
+
+
+def moe_get_device_error(ws: torch.Tensor) -> int:
+    out = ctypes.c_int32(0)
+    _check("moe_get_device_error", lib().moe_get_device_error(_ptr(ws), ctypes.byref(out), _stream()))
+    return int(out.value)
+
+
+def moe_gemm_set_group_m(group_m: int) -> None:
+    _check("moe_gemm_set_group_m", lib().moe_gemm_set_group_m(group_m))
+
+
+# --- device calls ----------------------------------------------------------------
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_ids: torch.Tensor, topk_weights: torch.Tensor):
+    assert logits.dtype == torch.float32 and logits.dim() == 2
+    T, E = logits.shape
+    assert topk_ids.dtype == torch.int32 and topk_ids.shape == (T, k)
+    assert topk_weights.dtype == torch.float32 and topk_weights.shape == (T, k)
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids),
+                                                  _ptr(topk_weights), _stream()))
+
+
+def moe_scatter_compact(x, topk_ids, expert_start, num_local_experts, block_e, rows_capacity,
+                        fp8, x_out, scale_out, m_indices, expert_start_loc, num_valid, src2dst, ws):
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    _check("moe_scatter_compact", lib().moe_scatter_compact(
+        _ptr(x), T, H, _ptr(topk_ids), k, expert_start, num_local_experts, block_e, rows_capacity,
+        _dtype_code(fp8), _ptr(x_out), _ptr(scale_out), _ptr(m_indices), _ptr(expert_start_loc),
+        _ptr(num_valid), _ptr(src2dst), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_scatter_masked(x, topk_ids, expert_start, num_local_experts, max_m, fp8, x_out, scale_out,
+                       masked_m, src2dst, ws):
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    _check("moe_scatter_masked", lib().moe_scatter_masked(
+        _ptr(x), T, H, _ptr(topk_ids), k, expert_start, num_local_experts, max_m, _dtype_code(fp8),
+        _ptr(x_out), _ptr(scale_out), _ptr(masked_m), _ptr(src2dst), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_quant_fp8_ue8m0(x, q, scale, m_indices=None):
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    _check("moe_quant_fp8_ue8m0", lib().moe_quant_fp8_ue8m0(
+        x.data_ptr(), M, K, x.stride(0), _ptr(m_indices), _ptr(q), _ptr(scale), _stream()))
+
+
+def moe_quant_weight_fp8_ue8m0(w, q, scale):
+    assert w.dtype == torch.bfloat16 and w.dim() == 3
+    G, N, K = w.shape
+    _check("moe_quant_weight_fp8_ue8m0", lib().moe_quant_weight_fp8_ue8m0(
+        _ptr(w), G, N, K, _ptr(q), _ptr(scale), _stream()))
+
+
+def grouped_gemm_contig(fp8, A, A_scale, B, B_scale, C, m_indices):
+    M, K = A.shape
+    G, N, K2 = B.shape
+    assert K == K2 and C.shape == (M, N) and C.dtype == torch.bfloat16
+    _check("grouped_gemm_contig", lib().grouped_gemm_contig(
+        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(m_indices),
+        M, N, K, G, _stream()))
+
+
+def grouped_gemm_masked(fp8, A, A_scale, B, B_scale, C, masked_m, expected_m):
+    G, max_m, K = A.shape
+    G2, N, K2 = B.shape
+    assert G == G2 and K == K2 and C.shape == (G, max_m, N) and C.dtype == torch.bfloat16
+    _check("grouped_gemm_masked", lib().grouped_gemm_masked(
+        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(masked_m),
+        expected_m, max_m, N, K, G, _stream()))
+
+
+def silu_and_mul(gateup, out, fp8=False, out_scale=None, m_indices=None, masked_m=None, max_m=0):
+    M, N = gateup.shape
+    _check("silu_and_mul", lib().silu_and_mul(
+        _ptr(gateup), M, N // 2, _ptr(m_indices), _ptr(masked_m), max_m, _dtype_code(fp8),
+        _ptr(out), _ptr(out_scale), _stream()))
+
+
+def moe_combine(Y, src2dst, topk_weights, out):
+    T, k = src2dst.shape
+    H = Y.shape[-1]
+    rows = Y.numel() // H
+    _check("moe_combine", lib().moe_combine(_ptr(Y), rows, _ptr(src2dst), _ptr(topk_weights), T, k,
+                                            H, _ptr(out), _stream()))

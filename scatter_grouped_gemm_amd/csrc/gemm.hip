@@ -1,0 +1,397 @@
+// Grouped NT GEMM for the expert layouts: C[r, :] = A[r, :] . B[g(r)]^T,
+// BF16 or FP8 e4m3 with UE8M0 scales, fp32 accumulation, bf16 output.
+//
+// Design (gfx950, wave64, 160 KB LDS):
+//   - One workgroup of 256 threads (4 wavefronts) computes a BM x BN tile of C.
+//     A k-stage is 128 bytes of every row (64 bf16 or 128 e4m3), staged in LDS
+//     with a 144-byte row pitch (16 bytes of padding keep the 16-lane fragment
+//     reads on distinct banks); two stages are double-buffered: the next
+//     stage's global loads are in flight while the current one is multiplied.
+//   - MFMA: v_mfma_f32_16x16x32_bf16 for BF16 and the block-scaled
+//     v_mfma_scale_f32_16x16x128_f8f6f4 for FP8.  The UE8M0 bytes are exactly
+//     the E8M0 scales that instruction consumes; the per-128-channel activation
+//     scale and the 128x128 weight-block scale are both constant over one
+//     128-wide k step, so every lane supplies its row's (column's) byte and no
+//     fp32 rescaling is done in the main loop.
+//   - The weight tile is the MFMA "A" operand and the activation tile the "B"
+//     operand, so the accumulator holds C^T: each lane owns 4 consecutive output
+//     columns of one row, which pack into one 8-byte LDS write in the epilogue;
+//     the tile then leaves LDS as 16-byte row-contiguous global stores.
+//   - Tiles never straddle experts: BM divides the 128-row alignment of the
+//     compact layout, so a tile's expert is the expert of its first row, and a
+//     tile whose first row is padding (-1) is skipped without loading anything.
+//     Masked tiles at or past masked_m[g] are skipped the same way.
+//   - Workgroup ids are remapped so that consecutive tiles run on one XCD (the
+//     hardware deals ids round-robin over the 8 XCDs, each with its own L2), and
+//     grouped so `group_m` M-tiles sweep the N-tiles together and share each
+//     weight panel while it is in L2.
+//   - Batch invariance: the instruction shape and the k order are the same for
+//     every tile size and layout; a row's result depends only on its own A row
+//     and its expert's weights.
+#include "common.cuh"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* A_scale;
+  const uint8_t* B;
+  const uint8_t* B_scale;
+  uint16_t* C;
+  const int32_t* rowinfo;  // m_indices (contiguous) or masked_m (masked)
+  int64_t M;               // contiguous: rows of A/C; masked: max_m
+  int N, K, G;
+  int m_tiles;             // contiguous: all M tiles; masked: M tiles per group
+  int n_tiles;
+  int total_m_tiles;       // contiguous: m_tiles; masked: G * m_tiles
+  int group_m;
+};
+
+constexpr int kLdsRow = 144;  // bytes per staged row (128 + 16 padding)
+
+template <int BM, int BN>
+constexpr int gemm_lds_bytes() {
+  return 2 * (BM + BN) * kLdsRow > BM * (BN * 2 + 16) ? 2 * (BM + BN) * kLdsRow : BM * (BN * 2 + 16);
+}
+
+template <int BM, int BN, bool FP8, bool MASKED>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) {
+  constexpr int WAVES_M = BM >= 128 ? 2 : 1;
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int A_STAGE = BM * kLdsRow;
+  constexpr int STAGE = (BM + BN) * kLdsRow;
+  constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte chunks per thread per stage
+  static_assert(BM % 32 == 0 && BN % 128 == 0 && WN <= 128, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_rowok[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  // ---- tile assignment -------------------------------------------------------
+  int pid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int per_group = p.group_m * p.n_tiles;
+  const int grp = pid / per_group;
+  const int first_m = grp * p.group_m;
+  const int gsz = min(p.total_m_tiles - first_m, p.group_m);
+  const int within = pid - grp * per_group;
+  const int mt = first_m + within % gsz;
+  const int nt = within / gsz;
+
+  int g;
+  int64_t row0;      // first row of the tile in A / C
+  int64_t row_last;  // last addressable row of this group (loads clamp to it)
+  int rows_here;     // masked: valid rows from row0
+  if (!MASKED) {
+    row0 = static_cast<int64_t>(mt) * BM;
+    g = p.rowinfo[row0];
+    if (g < 0 || g >= p.G) return;
+    row_last = p.M - 1;
+    rows_here = BM;
+  } else {
+    g = mt / p.m_tiles;
+    const int r_in0 = (mt - g * p.m_tiles) * BM;
+    int mm = p.rowinfo[g];
+    mm = mm < 0 ? 0 : (mm > p.M ? static_cast<int>(p.M) : mm);
+    if (r_in0 >= mm) return;
+    row0 = static_cast<int64_t>(g) * p.M + r_in0;
+    row_last = static_cast<int64_t>(g) * p.M + p.M - 1;
+    rows_here = mm - r_in0;
+  }
+  if (tid < BM) {
+    bool ok;
+    if (!MASKED) {
+      const int64_t r = row0 + tid;
+      ok = r < p.M && p.rowinfo[r] == g;
+    } else {
+      ok = tid < rows_here;
+    }
+    s_rowok[tid] = ok ? 1 : 0;
+  }
+
+  constexpr int ES = FP8 ? 1 : 2;
+  const int64_t rowbytes = static_cast<int64_t>(p.K) * ES;
+  const int nk = static_cast<int>(rowbytes / 128);
+
+  // ---- global -> LDS staging ------------------------------------------------------
+  const int chunk = tid & 7, lrow = tid >> 3;  // 8 x 16 B chunks per 128-byte row slice
+  const uint8_t* a_src[A_LD];
+  const uint8_t* b_src[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    int64_t r = row0 + lrow + 32 * i;
+    r = r > row_last ? row_last : r;
+    a_src[i] = p.A + r * rowbytes + chunk * 16;
+  }
+  const int64_t brow0 = static_cast<int64_t>(g) * p.N + static_cast<int64_t>(nt) * BN;
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) b_src[i] = p.B + (brow0 + lrow + 32 * i) * rowbytes + chunk * 16;
+
+  u32x4_t ra[A_LD], rb[B_LD];
+#define MOE_GLOAD(kt_)                                                                  \
+  do {                                                                                  \
+    const int64_t off_ = static_cast<int64_t>(kt_) * 128;                               \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] =                            \
+        *reinterpret_cast<const u32x4_t*>(a_src[i] + off_);                             \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) rb[i] =                            \
+        *reinterpret_cast<const u32x4_t*>(b_src[i] + off_);                             \
+  } while (0)
+#define MOE_LSTORE(s_)                                                                  \
+  do {                                                                                  \
+    uint8_t* base_ = smem + (s_) * STAGE + lrow * kLdsRow + chunk * 16;                 \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                                    \
+        *reinterpret_cast<u32x4_t*>(base_ + 32 * i * kLdsRow) = ra[i];                  \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                    \
+        *reinterpret_cast<u32x4_t*>(base_ + A_STAGE + 32 * i * kLdsRow) = rb[i];        \
+  } while (0)
+
+  // ---- FP8 scales -------------------------------------------------------------------
+  // activation scale of the lane's row in each of its TM sub-tiles; weight scale
+  // of the wave's 128-column block (uniform over the wave)
+  const uint8_t* as_src[TM];
+  const uint8_t* ws_src = nullptr;
+  int sa[TM], sa_next[TM], sw = 0, sw_next = 0;
+  if (FP8) {
+    const int KB = p.K / 128;
+    const int64_t gbase = MASKED ? static_cast<int64_t>(g) * KB * p.M - static_cast<int64_t>(g) * p.M : 0;
+#pragma unroll
+    for (int im = 0; im < TM; ++im) {
+      int64_t r = row0 + wm * WM + im * 16 + (lane & 15);
+      r = r > row_last ? row_last : r;
+      as_src[im] = p.A_scale + gbase + r;
+    }
+    const int nblk = (nt * BN + wn * WN) / 128;
+    ws_src = p.B_scale + (static_cast<int64_t>(g) * (p.N / 128) + nblk) * KB;
+  }
+#define MOE_SLOAD(kt_, dst_, dw_)                                                       \
+  do {                                                                                  \
+    const int64_t so_ = static_cast<int64_t>(kt_) * p.M;                                \
+    _Pragma("unroll") for (int im = 0; im < TM; ++im) dst_[im] = as_src[im][so_];       \
+    dw_ = ws_src[kt_];                                                                  \
+  } while (0)
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+    for (int im = 0; im < TM; ++im) acc[jn][im] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  MOE_GLOAD(0);
+  if (FP8) MOE_SLOAD(0, sa, sw);
+  MOE_LSTORE(0);
+  __syncthreads();
+
+  const int frag_row = lane & 15;
+  const int frag_k = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) {
+      MOE_GLOAD(kt + 1);
+      if (FP8) MOE_SLOAD(kt + 1, sa_next, sw_next);
+    }
+    const uint8_t* As = smem + s * STAGE;
+    const uint8_t* Bs = As + A_STAGE;
+    if (!FP8) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int koff = ks * 64 + frag_k * 16;
+        bf16x8_t af[TM], bf[TN];
+#pragma unroll
+        for (int im = 0; im < TM; ++im)
+          af[im] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + im * 16 + frag_row) * kLdsRow + koff);
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+          bf[jn] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WN + jn * 16 + frag_row) * kLdsRow + koff);
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+          for (int im = 0; im < TM; ++im)
+            acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[jn], af[im], acc[jn][im], 0, 0, 0);
+      }
+    } else {
+      const int koff = frag_k * 32;
+      i32x8_t af[TM], bf[TN];
+#pragma unroll
+      for (int im = 0; im < TM; ++im) {
+        const uint8_t* src = As + (wm * WM + im * 16 + frag_row) * kLdsRow + koff;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
+        af[im] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const uint8_t* src = Bs + (wn * WN + jn * 16 + frag_row) * kLdsRow + koff;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
+        bf[jn] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+        for (int im = 0; im < TM; ++im)
+          acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bf[jn], af[im], acc[jn][im], 0, 0, 0, sw, 0, sa[im]);
+    }
+    if (kt + 1 < nk) {
+      MOE_LSTORE(s ^ 1);
+      if (FP8) {
+#pragma unroll
+        for (int im = 0; im < TM; ++im) sa[im] = sa_next[im];
+        sw = sw_next;
+      }
+    }
+    __syncthreads();
+  }
+
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+#undef MOE_SLOAD
+  // ---- epilogue: accumulators -> bf16 tile in LDS -> row-contiguous stores ----------
+  constexpr int CROW = BN * 2 + 16;
+  uint8_t* Cs = smem;
+#pragma unroll
+  for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+    for (int im = 0; im < TM; ++im) {
+      const int m_local = wm * WM + im * 16 + frag_row;
+      const int n_local = wn * WN + jn * 16 + frag_k * 4;
+      const f32x4_t v = acc[jn][im];
+      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+      *reinterpret_cast<u32x2_t*>(Cs + m_local * CROW + n_local * 2) = u32x2_t{lo, hi};
+    }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte chunks per output row
+  uint16_t* Cg = p.C + row0 * p.N + static_cast<int64_t>(nt) * BN;
+  for (int idx = tid; idx < BM * CPR; idx += 256) {
+    const int rr = idx / CPR, cc = idx - rr * CPR;
+    if (s_rowok[rr])
+      *reinterpret_cast<u32x4_t*>(Cg + static_cast<int64_t>(rr) * p.N + cc * 8) =
+          *reinterpret_cast<const u32x4_t*>(Cs + rr * CROW + cc * 16);
+  }
+}
+
+template <int BM, int BN, bool FP8, bool MASKED>
+int32_t launch_gemm(GemmArgs a, hipStream_t s) {
+  constexpr int lds = gemm_lds_bytes<BM, BN>();
+  auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return MOE_EDEVICE;
+    attr_set = true;
+  }
+  a.n_tiles = a.N / BN;
+  if (MASKED) {
+    a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
+    a.total_m_tiles = a.G * a.m_tiles;
+  } else {
+    a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
+    a.total_m_tiles = a.m_tiles;
+  }
+  const int64_t grid = static_cast<int64_t>(a.total_m_tiles) * a.n_tiles;
+  if (grid == 0) return MOE_OK;
+  if (grid >= (1ll << 31)) return MOE_EINVAL;
+  if (a.group_m <= 0) a.group_m = 8;
+  kern<<<static_cast<int>(grid), 256, lds, s>>>(a);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+static int g_group_m = 8;
+
+}  // namespace moe
+
+using namespace moe;
+
+static int32_t validate_gemm(int32_t dtype, const void* A, const uint8_t* A_scale, const void* B,
+                             const uint8_t* B_scale, void* C, int32_t N, int32_t K, int32_t G) {
+  if (N <= 0 || K <= 0 || G <= 0) return MOE_EINVAL;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
+  if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
+  if (!A || !B || !C) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                       const void* B, const uint8_t* B_scale, void* C,
+                                       const int32_t* m_indices, int64_t M, int32_t N, int32_t K,
+                                       int32_t G, void* stream) {
+  if (M < 0) return MOE_EINVAL;
+  int32_t st = validate_gemm(dtype, A, A_scale, B, B_scale, C, N, K, G);
+  if (st != MOE_OK) return st;
+  if (M == 0) return MOE_OK;
+  if (!m_indices) return MOE_EINVAL;
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.A_scale = A_scale;
+  a.B = static_cast<const uint8_t*>(B);
+  a.B_scale = B_scale;
+  a.C = static_cast<uint16_t*>(C);
+  a.rowinfo = m_indices;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.G = G;
+  a.group_m = g_group_m;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if (N % 256 == 0)
+    return fp8 ? launch_gemm<128, 256, true, false>(a, s) : launch_gemm<128, 256, false, false>(a, s);
+  return fp8 ? launch_gemm<128, 128, true, false>(a, s) : launch_gemm<128, 128, false, false>(a, s);
+}
+
+extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                       const void* B, const uint8_t* B_scale, void* C,
+                                       const int32_t* masked_m, int32_t expected_m, int32_t max_m,
+                                       int32_t N, int32_t K, int32_t G, void* stream) {
+  if (max_m <= 0 || expected_m < 0) return MOE_EINVAL;
+  int32_t st = validate_gemm(dtype, A, A_scale, B, B_scale, C, N, K, G);
+  if (st != MOE_OK) return st;
+  if (!masked_m) return MOE_EINVAL;
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.A_scale = A_scale;
+  a.B = static_cast<const uint8_t*>(B);
+  a.B_scale = B_scale;
+  a.C = static_cast<uint16_t*>(C);
+  a.rowinfo = masked_m;
+  a.M = max_m;
+  a.N = N;
+  a.K = K;
+  a.G = G;
+  a.group_m = g_group_m;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  const bool n256 = N % 256 == 0;
+  // tile height from the hint: small expected counts waste less work on 32 rows
+  if (expected_m > 0 && expected_m <= 32) {
+    if (n256) return fp8 ? launch_gemm<32, 256, true, true>(a, s) : launch_gemm<32, 256, false, true>(a, s);
+    return fp8 ? launch_gemm<32, 128, true, true>(a, s) : launch_gemm<32, 128, false, true>(a, s);
+  }
+  if (expected_m > 0 && expected_m <= 64) {
+    if (n256) return fp8 ? launch_gemm<64, 256, true, true>(a, s) : launch_gemm<64, 256, false, true>(a, s);
+    return fp8 ? launch_gemm<64, 128, true, true>(a, s) : launch_gemm<64, 128, false, true>(a, s);
+  }
+  if (n256) return fp8 ? launch_gemm<128, 256, true, true>(a, s) : launch_gemm<128, 256, false, true>(a, s);
+  return fp8 ? launch_gemm<128, 128, true, true>(a, s) : launch_gemm<128, 128, false, true>(a, s);
+}
+
+// Tuning knob: M-tiles per N sweep in the tile order (does not change results).
+extern "C" int32_t moe_gemm_set_group_m(int32_t group_m) {
+  if (group_m <= 0) return MOE_EINVAL;
+  moe::g_group_m = group_m;
+  return MOE_OK;
+}

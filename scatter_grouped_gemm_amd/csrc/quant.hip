@@ -1,0 +1,204 @@
+// Per-token UE8M0 FP8 quantisation, 128x128 weight block quantisation and
+// SiLU-and-mul (with optional FP8 output).
+//
+// Row kernels use one wavefront per row: each lane owns 8 consecutive
+// channels (16 bytes of bf16), so 16 lanes hold one 128-channel group and the
+// group maximum is a 4-step butterfly inside those 16 lanes.
+#include "common.cuh"
+
+namespace moe {
+
+// Quantise the 8 values a lane holds (part of a 128-wide group spread over 16
+// lanes): returns the 8 e4m3 bytes packed little-endian; *e_out = exponent.
+__device__ __forceinline__ uint2 quant8_group16(const float (&f)[8], int* e_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = group_max<16>(amax);
+  const int e = ue8m0_exponent(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+  *e_out = e;
+  return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+    f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                         int K, int64_t ld_x,
+                                                         const int32_t* __restrict__ m_indices,
+                                                         uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;
+  if (m_indices && m_indices[r] < 0) return;
+  const uint16_t* xr = x + r * ld_x;
+  for (int col = lane * 8; col < K; col += 512) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(xr + col), f);
+    int e;
+    const uint2 qq = quant8_group16(f, &e);
+    *reinterpret_cast<uint2*>(q + r * K + col) = qq;
+    if ((lane & 15) == 0) scale[static_cast<int64_t>(col / 128) * M + r] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+// One workgroup per 128x128 block; thread t covers rows 8*(t/16) .. +8 and
+// columns 8*(t%16) .. +8 of the block.
+__global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t* __restrict__ w, int N,
+                                                           int K, uint8_t* __restrict__ q,
+                                                           uint8_t* __restrict__ scale) {
+  __shared__ float wmax[4];
+  const int nb = N / 128, kb = K / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t g = blk / (static_cast<int64_t>(nb) * kb);
+  const int bn = static_cast<int>((blk / kb) % nb), bk = static_cast<int>(blk % kb);
+  const int r0 = bn * 128 + (threadIdx.x >> 4) * 8;
+  const int c0 = bk * 128 + (threadIdx.x & 15) * 8;
+  const uint16_t* wg = w + g * N * static_cast<int64_t>(K);
+  float f[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    unpack8(*reinterpret_cast<const uint4*>(wg + static_cast<int64_t>(r0 + i) * K + c0), f[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[i][j]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = ue8m0_exponent(amax);
+  uint8_t* qg = q + g * N * static_cast<int64_t>(K);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i][j], -e)) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i][4 + j], -e)) << (8 * j);
+    *reinterpret_cast<uint2*>(qg + static_cast<int64_t>(r0 + i) * K + c0) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) scale[blk] = static_cast<uint8_t>(e + 127);
+}
+
+// SiLU-and-mul over one row per wavefront.  gate = first I columns, up = last I.
+template <bool FP8>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ gu, int64_t M,
+                                                       int I, const int32_t* __restrict__ m_indices,
+                                                       const int32_t* __restrict__ masked_m,
+                                                       int max_m, uint8_t* __restrict__ out,
+                                                       uint8_t* __restrict__ out_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;
+  if (m_indices && m_indices[r] < 0) return;
+  int64_t g = 0, rr = r;
+  if (masked_m) {
+    g = r / max_m;
+    rr = r - g * max_m;
+    if (rr >= masked_m[g]) return;
+  }
+  const uint16_t* row = gu + r * 2 * static_cast<int64_t>(I);
+  for (int col = lane * 8; col < I; col += 512) {
+    float gt[8], up[8], a[8];
+    unpack8(*reinterpret_cast<const uint4*>(row + col), gt);
+    unpack8(*reinterpret_cast<const uint4*>(row + I + col), up);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = gt[i] / (1.0f + expf(-gt[i]));
+      a[i] = bf16_to_f32(f32_to_bf16(s * up[i]));  // the bf16 activation
+    }
+    if (!FP8) {
+      *reinterpret_cast<uint4*>(out + (r * I + col) * 2) = pack8(a);
+    } else {
+      int e;
+      const uint2 qq = quant8_group16(a, &e);
+      *reinterpret_cast<uint2*>(out + r * I + col) = qq;
+      if ((lane & 15) == 0) {
+        const int b = col / 128;
+        const int64_t si = masked_m ? (g * (I / 128) + b) * max_m + rr : static_cast<int64_t>(b) * M + r;
+        out_scale[si] = static_cast<uint8_t>(e + 127);
+      }
+    }
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int32_t moe_quant_fp8_ue8m0(const void* x, int64_t M, int32_t K, int64_t ld_x,
+                                       const int32_t* m_indices, uint8_t* q, uint8_t* scale,
+                                       void* stream) {
+  if (M < 0 || K <= 0 || ld_x < K) return MOE_EINVAL;
+  if (K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!x || !q || !scale) return MOE_EINVAL;
+  const int64_t nb = (M + 3) / 4;
+  if (nb >= (1ll << 31)) return MOE_EINVAL;
+  quant_rows_kernel<<<static_cast<int>(nb), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), M, K, ld_x, m_indices, q, scale);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t N, int32_t K,
+                                              uint8_t* q, uint8_t* scale, void* stream) {
+  if (G < 0 || N <= 0 || K <= 0) return MOE_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (G == 0) return MOE_OK;
+  if (!w || !q || !scale) return MOE_EINVAL;
+  const int64_t blocks = static_cast<int64_t>(G) * (N / 128) * (K / 128);
+  if (blocks >= (1ll << 31)) return MOE_EINVAL;
+  quant_weight_kernel<<<static_cast<int>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(w), N, K, q, scale);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int32_t silu_and_mul(const void* gateup, int64_t M, int32_t I, const int32_t* m_indices,
+                                const int32_t* masked_m, int32_t max_m, int32_t out_dtype, void* out,
+                                uint8_t* out_scale, void* stream) {
+  if (M < 0 || I <= 0) return MOE_EINVAL;
+  if (I % 128 != 0) return MOE_EUNSUPPORTED;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
+  if (masked_m && m_indices) return MOE_EINVAL;
+  if (masked_m && (max_m <= 0 || M % max_m != 0)) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  if (!gateup || !out) return MOE_EINVAL;
+  if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && !out_scale) return MOE_EINVAL;
+  const int64_t nb = (M + 3) / 4;
+  if (nb >= (1ll << 31)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+    silu_mul_kernel<true><<<static_cast<int>(nb), 256, 0, s>>>(
+        static_cast<const uint16_t*>(gateup), M, I, m_indices, masked_m, max_m,
+        static_cast<uint8_t*>(out), out_scale);
+  else
+    silu_mul_kernel<false><<<static_cast<int>(nb), 256, 0, s>>>(
+        static_cast<const uint16_t*>(gateup), M, I, m_indices, masked_m, max_m,
+        static_cast<uint8_t*>(out), nullptr);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

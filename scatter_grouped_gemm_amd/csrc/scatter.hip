@@ -1,0 +1,391 @@
+// Scatter of routed tokens into the compact or masked expert layout.
+//
+// Deterministic and atomic-free on the value path: row positions come from
+// prefix sums, so the result is the same on every run.
+//   1. count  : each wavefront counts the local expert ids of one chunk of
+//               kChunk flat assignments (t*k + j) into per-chunk histograms.
+//   2. scan   : one workgroup turns the histograms into per-chunk offsets, the
+//               per-expert totals, padded sizes and expert start rows.
+//   3. rank   : each wavefront walks its chunk in order, 64 assignments at a
+//               time; lanes with the same expert are found with ballots and
+//               ranked by lane order, so rows follow increasing (t, j).  Writes
+//               src2dst.  (compact) m_indices is filled by a grid-stride pass.
+//   4. rows   : one workgroup per token reads its row once and writes it to
+//               each destination row, optionally quantised to e4m3 with
+//               per-128-channel UE8M0 scales.
+#include "common.cuh"
+
+namespace moe {
+
+constexpr int kChunk = 1024;   // assignments per wavefront chunk
+constexpr int kWsHeader = 256;  // bytes: device error word + padding
+
+struct ScatterWs {
+  int32_t* err;
+  int32_t* counts;  // [C][El]
+  int32_t* start;   // [El]
+  int32_t* total;   // [El]
+};
+
+__host__ __device__ inline int64_t num_chunks(int64_t A) { return (A + kChunk - 1) / kChunk; }
+
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+inline size_t ws_bytes(int64_t A, int El) {
+  return kWsHeader + align256(static_cast<size_t>(num_chunks(A)) * El * 4) +
+         2 * align256(static_cast<size_t>(El) * 4);
+}
+
+inline ScatterWs carve(void* ws, int64_t A, int El) {
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  ScatterWs w;
+  w.err = reinterpret_cast<int32_t*>(b);
+  b += kWsHeader;
+  w.counts = reinterpret_cast<int32_t*>(b);
+  b += align256(static_cast<size_t>(num_chunks(A)) * El * 4);
+  w.start = reinterpret_cast<int32_t*>(b);
+  b += align256(static_cast<size_t>(El) * 4);
+  w.total = reinterpret_cast<int32_t*>(b);
+  return w;
+}
+
+__global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __restrict__ ids,
+                                                            int64_t A, int expert_start, int El,
+                                                            int C, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ err) {
+  extern __shared__ int lds_i[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + w;
+  int* cnt = lds_i + w * El;
+  for (int e = lane; e < El; e += 64) cnt[e] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+  __syncthreads();
+  if (c < C) {
+    const int64_t a0 = static_cast<int64_t>(c) * kChunk;
+    const int64_t a1 = a0 + kChunk < A ? a0 + kChunk : A;
+    for (int64_t a = a0 + lane; a < a1; a += 64) {
+      const int e = ids[a] - expert_start;
+      if (e >= 0 && e < El) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  if (c < C)
+    for (int e = lane; e < El; e += 64) counts[static_cast<int64_t>(c) * El + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads, thread e owns expert e (El <= 1024).
+// counts become exclusive per-chunk offsets in place.
+__global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict__ counts, int C,
+                                                            int El, int block_e, int clamp,
+                                                            int32_t* __restrict__ start,
+                                                            int32_t* __restrict__ total,
+                                                            int32_t* __restrict__ start_out,
+                                                            int32_t* __restrict__ valid_out) {
+  __shared__ int64_t sh[1024];
+  const int e = threadIdx.x;
+  int64_t run = 0;
+  if (e < El) {
+    for (int c = 0; c < C; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * El + e;
+      const int v = counts[i];
+      counts[i] = static_cast<int32_t>(run);
+      run += v;
+    }
+  }
+  const int64_t padded = e < El ? (run + block_e - 1) / block_e * block_e : 0;
+  sh[e] = padded;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 1024 entries
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t v = e >= off ? sh[e - off] : 0;
+    __syncthreads();
+    sh[e] += v;
+    __syncthreads();
+  }
+  if (e < El) {
+    const int32_t st = static_cast<int32_t>(sh[e] - padded);
+    start[e] = st;
+    total[e] = static_cast<int32_t>(run);
+    if (start_out) start_out[e] = st;
+    if (valid_out) valid_out[e] = static_cast<int32_t>(clamp > 0 && run > clamp ? clamp : run);
+  }
+}
+
+template <bool MASKED>
+__global__ __launch_bounds__(256) void scatter_rank_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int expert_start, int El, int C,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ start, int max_m,
+    int32_t* __restrict__ src2dst, int32_t* __restrict__ err) {
+  extern __shared__ int lds_i[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + w;
+  if (c >= C) return;  // whole wavefront
+  int* base = lds_i + w * El;
+  for (int e = lane; e < El; e += 64)
+    base[e] = offsets[static_cast<int64_t>(c) * El + e] + (MASKED ? 0 : start[e]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int bits = 32 - __clz(El);  // enough bits for the sentinel value El
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int64_t a0 = static_cast<int64_t>(c) * kChunk;
+  for (int s = 0; s < kChunk; s += 64) {
+    const int64_t a = a0 + s + lane;
+    const bool valid = a < A;
+    int e = valid ? ids[a] - expert_start : -1;
+    const bool local = valid && e >= 0 && e < El;
+    const int key = local ? e : El;
+    uint64_t mask = ballot(true);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(mask & below);
+    const int cnt = __popcll(mask);
+    int r = 0;
+    if (local) r = base[key] + rank;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (local && rank == 0) base[key] = r + cnt;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      int out = -1;
+      if (local) {
+        if (!MASKED) {
+          out = r;
+        } else if (r < max_m) {
+          out = key * max_m + r;
+        } else {
+          atomicOr(err, MOE_DEVERR_MASKED_OVERFLOW);
+        }
+      }
+      src2dst[a] = out;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_m_indices_kernel(const int32_t* __restrict__ start,
+                                                             const int32_t* __restrict__ total,
+                                                             int El, int64_t R,
+                                                             int32_t* __restrict__ m_indices) {
+  __shared__ int s_start[1024];
+  __shared__ int s_total[1024];
+  for (int e = threadIdx.x; e < El; e += blockDim.x) {
+    s_start[e] = start[e];
+    s_total[e] = total[e];
+  }
+  __syncthreads();
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < R;
+       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    // last expert whose block starts at or before r (empty experts share the
+    // start of the next one, so the last of equal starts owns the rows)
+    int lo = 0, hi = El - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_start[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    m_indices[r] = (r - s_start[lo] < s_total[lo]) ? lo : -1;
+  }
+}
+
+// Destination scale index of row `row`, 128-channel block b.
+__device__ __forceinline__ int64_t scale_index(int64_t row, int b, int64_t ld, int max_m, int HB) {
+  if (max_m == 0) return static_cast<int64_t>(b) * ld + row;
+  const int64_t g = row / max_m;
+  return (g * HB + b) * max_m + (row - g * max_m);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(
+    const uint16_t* __restrict__ x, int H, int k, const int32_t* __restrict__ src2dst,
+    uint8_t* __restrict__ x_out, uint8_t* __restrict__ scale_out, int64_t scale_ld, int max_m) {
+  __shared__ int rows[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) rows[threadIdx.x] = src2dst[static_cast<int64_t>(t) * k + threadIdx.x];
+  __syncthreads();
+  const uint16_t* xt = x + static_cast<int64_t>(t) * H;
+  const int HB = H / 128;
+  for (int col = threadIdx.x * 8; col < H; col += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + col);
+    if (!FP8) {
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r >= 0) *reinterpret_cast<uint4*>(x_out + (static_cast<int64_t>(r) * H + col) * 2) = v;
+      }
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float f[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+        f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+        amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+      }
+      amax = group_max<16>(amax);
+      const int e = ue8m0_exponent(amax);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+      const uint2 q = make_uint2(lo, hi);
+      const bool leader = (threadIdx.x & 15) == 0;
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r < 0) continue;
+        *reinterpret_cast<uint2*>(x_out + static_cast<int64_t>(r) * H + col) = q;
+        if (leader) scale_out[scale_index(r, col / 128, scale_ld, max_m, HB)] = static_cast<uint8_t>(e + 127);
+      }
+    }
+  }
+}
+
+int32_t validate_common(const void* x, int32_t T, int32_t H, const int32_t* ids, int32_t k,
+                        int32_t El, int32_t out_dtype, void* x_out, const uint8_t* scale_out,
+                        int32_t* src2dst, void* ws, size_t ws_bytes_given) {
+  if (T < 0 || H <= 0 || k < 1 || k > 32 || El < 1 || El > 1024) return MOE_EINVAL;
+  if (static_cast<int64_t>(T) * k >= (1ll << 31)) return MOE_EINVAL;
+  if (H % 128 != 0) return MOE_EUNSUPPORTED;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
+  if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && !scale_out) return MOE_EINVAL;
+  if (!ws || ws_bytes_given < ws_bytes(static_cast<int64_t>(T) * k, El)) return MOE_ECAPACITY;
+  if (T > 0 && (!x || !ids || !x_out || !src2dst)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts) {
+  if (T < 0 || k < 1 || num_local_experts < 1) return 0;
+  return ws_bytes(static_cast<int64_t>(T) * k, num_local_experts);
+}
+
+extern "C" int64_t moe_compact_rows_bound(int64_t A, int32_t E, int32_t block_e) {
+  if (A < 0 || E <= 0 || block_e <= 0) return -1;
+  const int64_t n = A < E ? A : E;
+  return static_cast<int64_t>(block_e) * (n + (A - n) / block_e);
+}
+
+extern "C" int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_experts) {
+  return (num_experts > num_local_experts && num_local_experts <= 32) ? 1 : 0;
+}
+
+static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start, int32_t El,
+                            int32_t block_e, const ScatterWs& w, int32_t* start_out,
+                            int32_t* valid_out, bool masked, int32_t max_m, int32_t* src2dst,
+                            hipStream_t s) {
+  const int C = static_cast<int>(num_chunks(A));
+  const int nb = (C + 3) / 4;
+  const size_t lds = static_cast<size_t>(4) * El * sizeof(int);
+  if (C > 0) {
+    scatter_count_kernel<<<nb, 256, lds, s>>>(ids, A, expert_start, El, C, w.counts, w.err);
+  } else {
+    scatter_count_kernel<<<1, 256, lds, s>>>(ids, 0, expert_start, El, 0, w.counts, w.err);
+  }
+  MOE_CHECK_LAUNCH();
+  scatter_scan_kernel<<<1, 1024, 0, s>>>(w.counts, C, El, masked ? 1 : block_e, masked ? max_m : 0,
+                                         w.start, w.total, start_out, valid_out);
+  MOE_CHECK_LAUNCH();
+  if (C > 0) {
+    if (masked)
+      scatter_rank_kernel<true><<<nb, 256, lds, s>>>(ids, A, expert_start, El, C, w.counts,
+                                                     w.start, max_m, src2dst, w.err);
+    else
+      scatter_rank_kernel<false><<<nb, 256, lds, s>>>(ids, A, expert_start, El, C, w.counts,
+                                                      w.start, 0, src2dst, w.err);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                                       int32_t k, int32_t expert_start, int32_t El,
+                                       int32_t block_e, int64_t rows_capacity, int32_t out_dtype,
+                                       void* x_out, uint8_t* scale_out, int32_t* m_indices,
+                                       int32_t* expert_start_loc, int32_t* num_valid,
+                                       int32_t* src2dst, void* ws, size_t ws_bytes_given,
+                                       void* stream) {
+  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst, ws,
+                               ws_bytes_given);
+  if (st != MOE_OK) return st;
+  if (block_e <= 0 || block_e % 128 != 0) return MOE_EUNSUPPORTED;
+  if (!expert_start_loc || !num_valid || (rows_capacity > 0 && !m_indices)) return MOE_EINVAL;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (rows_capacity < moe_compact_rows_bound(A, El, block_e)) return MOE_ECAPACITY;
+  if (rows_capacity >= (1ll << 31)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ScatterWs w = carve(ws, A, El);
+  st = launch_front(topk_ids, A, expert_start, El, block_e, w, expert_start_loc, num_valid, false, 0,
+                    src2dst, s);
+  if (st != MOE_OK) return st;
+  if (rows_capacity > 0) {
+    int64_t nb = (rows_capacity + 255) / 256;
+    if (nb > 2048) nb = 2048;
+    fill_m_indices_kernel<<<static_cast<int>(nb), 256, 0, s>>>(w.start, w.total, El, rows_capacity,
+                                                               m_indices);
+    MOE_CHECK_LAUNCH();
+  }
+  if (T > 0) {
+    if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+      scatter_rows_kernel<true><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
+                                                  static_cast<uint8_t*>(x_out), scale_out,
+                                                  rows_capacity, 0);
+    else
+      scatter_rows_kernel<false><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
+                                                   static_cast<uint8_t*>(x_out), nullptr, 0, 0);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_scatter_masked(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                                      int32_t k, int32_t expert_start, int32_t El, int32_t max_m,
+                                      int32_t out_dtype, void* x_out, uint8_t* scale_out,
+                                      int32_t* masked_m, int32_t* src2dst, void* ws,
+                                      size_t ws_bytes_given, void* stream) {
+  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst, ws,
+                               ws_bytes_given);
+  if (st != MOE_OK) return st;
+  if (!masked_m || max_m <= 0) return MOE_EINVAL;
+  if (max_m < T) return MOE_ECAPACITY;
+  if (static_cast<int64_t>(El) * max_m >= (1ll << 31)) return MOE_EINVAL;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ScatterWs w = carve(ws, A, El);
+  st = launch_front(topk_ids, A, expert_start, El, 1, w, nullptr, masked_m, true, max_m, src2dst, s);
+  if (st != MOE_OK) return st;
+  if (T > 0) {
+    if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+      scatter_rows_kernel<true><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
+                                                  static_cast<uint8_t*>(x_out), scale_out, 0, max_m);
+    else
+      scatter_rows_kernel<false><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
+                                                   static_cast<uint8_t*>(x_out), nullptr, 0, max_m);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_get_device_error(const void* ws, int32_t* host_err, void* stream) {
+  if (!ws || !host_err) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host_err, ws, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MOE_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_EDEVICE;
+  return MOE_OK;
+}
+
+extern "C" const char* moe_status_str(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported dtype or alignment";
+    case MOE_ECAPACITY: return "buffer below the required capacity";
+    case MOE_EDEVICE: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}

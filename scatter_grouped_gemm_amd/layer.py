@@ -1,0 +1,193 @@
+"""The MoE expert path as one layer over libmoe's C calls.
+
+forward(x, logits):  route -> scatter (compact or masked; FP8: fused UE8M0
+quant) -> w13 grouped GEMM -> SiLU-and-mul (FP8: fused requant) -> w2 grouped
+GEMM -> weighted combine.  Every buffer has a static shape fixed at
+construction from (max_tokens, k, num_local_experts, block_e), so a forward
+never reads device data back to the host and can be captured in a HIP graph.
+
+Layout choice follows "Support DeepGEMM for standard MoE dispatch",
+implementation breakdown item 2: masked when there are non-local experts and at
+most 32 local ones, otherwise compact (``layout="auto"``).  The activation dtype
+follows the weights ("[Feature] Support BF16 and batch-invariant inference
+with DeepEP v2", implementation breakdown item 2): FP8 weights make the path
+FP8, and asking for the other dtype is an error.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, *, hidden: int, intermediate: int, num_experts: int, top_k: int,
+                 max_tokens: int, num_local_experts: int | None = None, expert_start: int = 0,
+                 fp8: bool = False, layout: str = "auto", block_e: int = 128,
+                 max_m: int | None = None, expected_m: int = 0, device="cuda"):
+        self.H, self.I, self.E, self.k = hidden, intermediate, num_experts, top_k
+        self.El = num_local_experts or num_experts
+        self.expert_start = expert_start
+        self.fp8 = fp8
+        self.block_e = block_e
+        self.T_max = max_tokens
+        self.device = torch.device(device)
+        if layout == "auto":
+            layout = "masked" if L.moe_use_masked_layout(self.E, self.El) else "compact"
+        if layout not in ("compact", "masked"):
+            raise ValueError(f"unknown layout {layout!r}")
+        self.layout = layout
+        self.max_m = max_m if max_m is not None else max_tokens
+        self.expected_m = expected_m
+        d, T, H, I, El, k = self.device, max_tokens, hidden, intermediate, self.El, top_k
+        if layout == "compact":
+            self.rows = L.moe_compact_rows_bound(T * k, El, block_e)
+        else:
+            self.rows = El * self.max_m
+        R = self.rows
+        adt = torch.uint8 if fp8 else torch.bfloat16
+        # static buffers (uninitialised: every valid row is written before it is read)
+        self.topk_ids = torch.empty(T, k, dtype=torch.int32, device=d)
+        self.topk_weights = torch.empty(T, k, dtype=torch.float32, device=d)
+        self.src2dst = torch.empty(T, k, dtype=torch.int32, device=d)
+        self.x_buf = torch.empty(R, H, dtype=adt, device=d)
+        self.x_scale = torch.empty(R * (H // 128), dtype=torch.uint8, device=d) if fp8 else None
+        self.gateup = torch.empty(R, 2 * I, dtype=torch.bfloat16, device=d)
+        self.act = torch.empty(R, I, dtype=adt, device=d)
+        self.act_scale = torch.empty(R * (I // 128), dtype=torch.uint8, device=d) if fp8 else None
+        self.y = torch.empty(R, H, dtype=torch.bfloat16, device=d)
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device=d)
+        if layout == "compact":
+            self.m_indices = torch.empty(R, dtype=torch.int32, device=d)
+            self.expert_start_loc = torch.empty(El, dtype=torch.int32, device=d)
+            self.num_valid = torch.empty(El, dtype=torch.int32, device=d)
+            self.masked_m = None
+        else:
+            self.m_indices = None
+            self.masked_m = torch.empty(El, dtype=torch.int32, device=d)
+        ws_bytes = L.moe_scatter_ws_bytes(T, k, El)
+        self.ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.int32, device=d)
+        self.w13 = self.w2 = self.w13_scale = self.w2_scale = None
+        # optional timing: name -> list of (start, end) HIP events recorded on
+        # the current stream around each step of forward()
+        self.marks = None
+
+    def _mark(self, name):
+        if self.marks is None:
+            return _NoMark()
+        return _Mark(self.marks.setdefault(name, []))
+
+    # -- weights ---------------------------------------------------------------------
+
+    def allocate_weights(self):
+        d, El, H, I = self.device, self.El, self.H, self.I
+        wdt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.w13 = torch.empty(El, 2 * I, H, dtype=wdt, device=d)
+        self.w2 = torch.empty(El, H, I, dtype=wdt, device=d)
+        if self.fp8:
+            self.w13_scale = torch.empty(El, 2 * I // 128, H // 128, dtype=torch.uint8, device=d)
+            self.w2_scale = torch.empty(El, H // 128, I // 128, dtype=torch.uint8, device=d)
+
+    def set_expert(self, e: int, w13: torch.Tensor, w2: torch.Tensor):
+        """Load local expert e from bf16 weights ([2I, H] and [H, I]); FP8 layers
+        quantise them to 128x128 blocks with UE8M0 scales in the library."""
+        if self.w13 is None:
+            self.allocate_weights()
+        if not self.fp8:
+            self.w13[e].copy_(w13)
+            self.w2[e].copy_(w2)
+            return
+        L.moe_quant_weight_fp8_ue8m0(w13.contiguous()[None], self.w13[e:e + 1], self.w13_scale[e:e + 1])
+        L.moe_quant_weight_fp8_ue8m0(w2.contiguous()[None], self.w2[e:e + 1], self.w2_scale[e:e + 1])
+
+    def set_weights(self, w13: torch.Tensor, w2: torch.Tensor):
+        for e in range(self.El):
+            self.set_expert(e, w13[e], w2[e])
+
+    def set_quantized_weights(self, w13q, w13s, w2q, w2s):
+        """Take already block-quantised FP8 weights (e4m3 bytes + UE8M0 bytes)."""
+        if not self.fp8:
+            raise ValueError("FP8 weights given to a BF16 layer: the activation dtype follows the weights")
+        self.w13, self.w13_scale, self.w2, self.w2_scale = w13q, w13s, w2q, w2s
+
+    # -- forward ----------------------------------------------------------------------
+
+    def route(self, logits: torch.Tensor):
+        T = logits.shape[0]
+        L.moe_route_topk(logits, self.k, self.topk_ids[:T], self.topk_weights[:T])
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None, *,
+                topk_ids: torch.Tensor | None = None, topk_weights: torch.Tensor | None = None):
+        T = x.shape[0]
+        if T > self.T_max:
+            raise ValueError(f"{T} tokens exceed the layer's static capacity {self.T_max}")
+        if topk_ids is None:
+            with self._mark("route"):
+                self.route(logits)
+            ids, tw = self.topk_ids[:T], self.topk_weights[:T]
+        else:
+            ids, tw = topk_ids, topk_weights
+        s2d = self.src2dst[:T]
+        fp8 = self.fp8
+        I = self.I
+        if self.layout == "compact":
+            with self._mark("scatter"):
+                L.moe_scatter_compact(x, ids, self.expert_start, self.El, self.block_e, self.rows,
+                                      fp8, self.x_buf, self.x_scale, self.m_indices,
+                                      self.expert_start_loc, self.num_valid, s2d, self.ws)
+            with self._mark("gemm_w13"):
+                L.grouped_gemm_contig(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
+                                      self.gateup, self.m_indices)
+            with self._mark("silu_and_mul"):
+                L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, m_indices=self.m_indices)
+            with self._mark("gemm_w2"):
+                L.grouped_gemm_contig(fp8, self.act, self.act_scale, self.w2, self.w2_scale, self.y,
+                                      self.m_indices)
+        else:
+            El, mm = self.El, self.max_m
+            with self._mark("scatter"):
+                L.moe_scatter_masked(x, ids, self.expert_start, El, mm, fp8, self.x_buf,
+                                     self.x_scale, self.masked_m, s2d, self.ws)
+            with self._mark("gemm_w13"):
+                L.grouped_gemm_masked(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
+                                      self.w13, self.w13_scale, self.gateup.view(El, mm, 2 * I),
+                                      self.masked_m, self.expected_m)
+            with self._mark("silu_and_mul"):
+                L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, masked_m=self.masked_m,
+                               max_m=mm)
+            with self._mark("gemm_w2"):
+                L.grouped_gemm_masked(fp8, self.act.view(El, mm, I), self.act_scale, self.w2,
+                                      self.w2_scale, self.y.view(El, mm, self.H), self.masked_m,
+                                      self.expected_m)
+        out = self.out[:T]
+        with self._mark("combine"):
+            L.moe_combine(self.y, s2d, tw, out)
+        return out
+
+    __call__ = forward
+
+
+class _NoMark:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+class _Mark:
+    """Records a (start, end) pair of HIP events on the current stream."""
+
+    def __init__(self, sink):
+        self.sink = sink
+
+    def __enter__(self):
+        self.start = torch.cuda.Event(enable_timing=True)
+        self.end = torch.cuda.Event(enable_timing=True)
+        self.start.record()
+        return self
+
+    def __exit__(self, *a):
+        self.end.record()
+        self.sink.append((self.start, self.end))
+        return False

@@ -1,0 +1,112 @@
+"""The C ABI on the host: every symbol declared in include/moe.h is exported by
+libmoe.so, the pure host helpers agree with the oracle, and argument
+validation rejects bad calls before any device work (no GPU needed: every call
+here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from scatter_grouped_gemm_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 4096  # a non-null address that is never dereferenced: each call below fails validation
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", L.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+        assert n in L.SIGNATURES, n
+        getattr(L.lib(), n)
+
+
+def test_host_helpers_match_oracle(orc):
+    for A, E, B in [(0, 8, 128), (128, 8, 128), (8192, 8, 128), (65536, 256, 128), (7, 128, 128),
+                    (131072, 128, 128), (5, 3, 256)]:
+        assert L.moe_compact_rows_bound(A, E, B) == orc.compact_rows_bound(A, E, B)
+    for E, El in [(256, 32), (256, 33), (8, 8), (64, 1), (32, 32)]:
+        assert L.moe_use_masked_layout(E, El) == orc.use_masked_layout(E, El)
+    assert L.lib().moe_compact_rows_bound(-1, 8, 128) == -1
+    assert L.lib().moe_compact_rows_bound(10, 0, 128) == -1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert L.status_str(s)
+    assert L.status_str(99) == "unknown status"
+
+
+def test_ws_bytes_grow_with_problem():
+    a = L.moe_scatter_ws_bytes(64, 2, 8)
+    b = L.moe_scatter_ws_bytes(16384, 8, 128)
+    assert 0 < a < b
+    assert L.lib().moe_scatter_ws_bytes(-1, 2, 8) == 0
+
+
+def test_validation_rejects_before_launch():
+    lib = L.lib()
+    P = FAKE
+    # routing
+    assert lib.moe_route_topk(P, 4, 0, 2, P, P, None) == L.MOE_EINVAL          # E = 0
+    assert lib.moe_route_topk(P, 4, 8, 9, P, P, None) == L.MOE_EINVAL          # k > E
+    assert lib.moe_route_topk(P, 4, 2048, 8, P, P, None) == L.MOE_EINVAL       # E > 1024
+    assert lib.moe_route_topk(None, 4, 8, 2, P, P, None) == L.MOE_EINVAL
+    ws = L.moe_scatter_ws_bytes(64, 2, 8)
+    # compact scatter: capacity below the bound, H not a multiple of 128, block_e, ws too small
+    bound = L.moe_compact_rows_bound(128, 8, 128)
+    args = lambda T, H, El, be, R, dt, wsb: (P, T, H, P, 2, 0, El, be, R, dt, P, P, P, P, P, P, P, wsb, None)
+    assert lib.moe_scatter_compact(*args(64, 256, 8, 128, bound - 1, 0, ws)) == L.MOE_ECAPACITY
+    assert lib.moe_scatter_compact(*args(64, 200, 8, 128, bound, 0, ws)) == L.MOE_EUNSUPPORTED
+    assert lib.moe_scatter_compact(*args(64, 256, 8, 64, bound, 0, ws)) == L.MOE_EUNSUPPORTED
+    assert lib.moe_scatter_compact(*args(64, 256, 8, 128, bound, 0, ws - 1)) == L.MOE_ECAPACITY
+    assert lib.moe_scatter_compact(*args(64, 256, 8, 128, bound, 7, ws)) == L.MOE_EUNSUPPORTED
+    assert lib.moe_scatter_compact(*args(64, 256, 2000, 128, bound, 0, ws)) == L.MOE_EINVAL
+    assert lib.moe_scatter_compact(P, 64, 256, P, 2, 0, 8, 128, bound, 1, P, None, P, P, P, P, P, ws,
+                                   None) == L.MOE_EINVAL                       # FP8 without scales
+    # masked scatter: max_m below T
+    assert lib.moe_scatter_masked(P, 64, 256, P, 2, 0, 8, 63, 0, P, P, P, P, P, ws, None) == L.MOE_ECAPACITY
+    assert lib.moe_scatter_masked(P, 64, 256, P, 2, 0, 8, 64, 0, P, P, None, P, P, ws, None) == L.MOE_EINVAL
+    # quantisation
+    assert lib.moe_quant_fp8_ue8m0(P, 4, 100, 100, None, P, P, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_quant_fp8_ue8m0(P, 4, 128, 64, None, P, P, None) == L.MOE_EINVAL
+    assert lib.moe_quant_weight_fp8_ue8m0(P, 2, 128, 96, P, P, None) == L.MOE_EUNSUPPORTED
+    # grouped GEMMs: dtype follows the weights -> FP8 without scales is an error
+    assert lib.grouped_gemm_contig(1, P, None, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(1, P, P, P, None, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(0, P, None, P, None, P, P, 256, 200, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(0, P, None, P, None, P, P, 256, 256, 100, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(5, P, None, P, None, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(0, P, None, P, None, P, None, 256, 256, 256, 2, None) == L.MOE_EINVAL
+    assert lib.grouped_gemm_contig(0, P, None, P, None, P, P, -1, 256, 256, 2, None) == L.MOE_EINVAL
+    assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 8, 0, 256, 256, 2, None) == L.MOE_EINVAL
+    assert lib.grouped_gemm_masked(1, P, None, P, P, P, P, 8, 64, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    # SiLU-and-mul and combine
+    assert lib.silu_and_mul(P, 16, 100, None, None, 0, 0, P, None, None) == L.MOE_EUNSUPPORTED
+    assert lib.silu_and_mul(P, 16, 128, None, None, 0, 1, P, None, None) == L.MOE_EINVAL
+    assert lib.silu_and_mul(P, 16, 128, P, P, 8, 0, P, None, None) == L.MOE_EINVAL
+    assert lib.silu_and_mul(P, 15, 128, None, P, 8, 0, P, None, None) == L.MOE_EINVAL
+    assert lib.moe_combine(P, 10, P, P, 4, 33, 256, P, None) == L.MOE_EINVAL
+    assert lib.moe_combine(P, 10, P, P, 4, 2, 100, P, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_gemm_set_group_m(0) == L.MOE_EINVAL
+
+
+def test_empty_calls_are_no_ops():
+    """Zero-sized work returns OK without touching the device."""
+    lib = L.lib()
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == L.MOE_OK
+    assert lib.moe_quant_fp8_ue8m0(None, 0, 128, 128, None, None, None, None) == L.MOE_OK
+    assert lib.grouped_gemm_contig(0, FAKE, None, FAKE, None, FAKE, None, 0, 256, 256, 2, None) == L.MOE_OK
+    assert lib.moe_combine(None, 0, None, None, 0, 2, 256, None, None) == L.MOE_OK
