@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic tokens already
+resident in HBM: top-k routing -> scatter into the expert layout (FP8: fused
+UE8M0 quantisation) -> w13 grouped GEMM -> SiLU-and-mul (FP8: fused requant)
+-> w2 grouped GEMM -> weighted combine.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is the FP8 DeepSeek-V3-shaped prefill (T=8192, H=7168,
+I=2048, 256 experts, top-8, 128x128 block-scaled e4m3 weights).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (BF16/FP8) as % of MFMA peak, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp8_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = default)")
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
+    return ap.parse_args()
+
+
+def build_layer(wl, torch):
+    from scatter_grouped_gemm_amd import MoELayer, inputs
+    layer = MoELayer(hidden=wl.H, intermediate=wl.I, num_experts=wl.E, top_k=wl.k, max_tokens=wl.T,
+                     num_local_experts=wl.El, expert_start=wl.expert_start, fp8=wl.fp8,
+                     layout=wl.layout, block_e=wl.block_e, max_m=wl.max_m or None,
+                     expected_m=wl.expected_m, device="cuda")
+    t0 = time.time()
+    for e in range(wl.El):
+        w13, w2 = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
+        layer.set_expert(e, w13, w2)
+        del w13, w2
+    torch.cuda.synchronize()
+    log(f"weights ready for {wl.El} experts in {time.time() - t0:.1f}s")
+    x = inputs.tokens(wl, "cuda")
+    logits = inputs.logits(wl, "cuda")
+    return layer, x, logits
+
+
+def gemm_work(wl, layer, torch):
+    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs for the valid
+    rows of this batch (padding rows excluded)."""
+    if layer.layout == "compact":
+        counts = layer.num_valid.cpu().to(torch.int64)
+    else:
+        counts = layer.masked_m.cpu().to(torch.int64)
+    A = int(counts.sum())
+    active = int((counts > 0).sum())
+    ab = 1 if wl.fp8 else 2
+    H, I = wl.H, wl.I
+    w13_flops = 2.0 * A * (2 * I) * H
+    w2_flops = 2.0 * A * H * I
+    sc = (1.0 / (128 * 128)) if wl.fp8 else 0.0          # weight block scales
+    asc = (1.0 / 128) if wl.fp8 else 0.0                 # activation scales
+    w13_bytes = active * 2 * I * H * (ab + sc) + A * H * (ab + asc) + A * 2 * I * 2
+    w2_bytes = active * H * I * (ab + sc) + A * I * (ab + asc) + A * H * 2
+    return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
+                w13_bytes=w13_bytes, w2_bytes=w2_bytes)
+
+
+def roofline(flops, nbytes, ms, dtype):
+    peak_f = PEAK_TFLOPS[dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = flops / nbytes
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if ai < ridge:
+        return dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                    tflops=round(tflops, 1), mfma_frac=round(tflops / peak_f, 4),
+                    arithmetic_intensity=round(ai, 1))
+    return dict(bound="mfma", achieved=round(tflops, 1), peak=peak_f, unit="TFLOP/s",
+                frac=round(tflops / peak_f, 4), traffic=None, gbs=round(gbs, 1),
+                arithmetic_intensity=round(ai, 1))
+
+
+def cpu_baseline(wl, x, logits, n_tok, torch):
+    """The oracle, as it stands, on the first n_tok tokens of the same batch:
+    routing plus the layout-free per-token expert path (w13 -> SiLU-mul ->
+    (requant) -> w2 -> weighted sum), timed on the host cores.  Weight
+    preparation (copying the needed experts' bf16 weights and, for FP8, the
+    oracle's own 128x128 block quantisation) is not timed, as it is not part of
+    a step on the GPU either."""
+    import numpy as np
+
+    import oracle
+    from scatter_grouped_gemm_amd import inputs
+    oracle.build(force=False)
+    xs = inputs.bf16_bits(x[:n_tok])
+    ls = logits[:n_tok].cpu().numpy()
+    ids, w = oracle.route_topk(ls, wl.k)
+    local = ids - wl.expert_start
+    need = sorted({int(e) for e in local.reshape(-1) if 0 <= e < wl.El})
+    remap = {e: i for i, e in enumerate(need)}
+    t0 = time.time()
+    w13s, w2s = [], []
+    for e in need:
+        a, b = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
+        a, b = inputs.bf16_bits(a)[None], inputs.bf16_bits(b)[None]
+        if wl.fp8:
+            a, b = oracle.quant_weight_blocks(a), oracle.quant_weight_blocks(b)
+        w13s.append(a)
+        w2s.append(b)
+    log(f"oracle weights for {len(need)} experts prepared in {time.time() - t0:.1f}s")
+    ids_c = np.where((local >= 0) & (local < wl.El),
+                     np.vectorize(lambda e: remap.get(int(e), -1))(local), -1).astype(np.int32)
+    if wl.fp8:
+        W = dict(w13q=np.concatenate([a[0] for a in w13s]), w13s=np.concatenate([a[1] for a in w13s]),
+                 w2q=np.concatenate([a[0] for a in w2s]), w2s=np.concatenate([a[1] for a in w2s]))
+    else:
+        W = dict(w13=np.concatenate(w13s), w2=np.concatenate(w2s))
+    t0 = time.perf_counter()
+    ids2, w2_ = oracle.route_topk(ls, wl.k)
+    out = oracle.moe_dense(xs, ids_c, w2_, 0, len(need), wl.fp8, **W)
+    dt = time.perf_counter() - t0
+    assert np.array_equal(ids2, ids) and out.shape == (n_tok, wl.H)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return dict(value=round(n_tok / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"first {n_tok} tokens of the batch: routing + per-token expert path "
+                       f"({len(need)} experts), {dt:.1f}s on {cores} threads")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the expert path on a single MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from scatter_grouped_gemm_amd import _lib, inputs
+    wl = inputs.get(args.workload)
+    if args.group_m:
+        _lib.moe_gemm_set_group_m(args.group_m)
+    log(f"workload {wl.name}")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del a, b
+    layer, x, logits = build_layer(wl, torch)
+    for _ in range(args.warmup):
+        layer(x, logits)
+    torch.cuda.synchronize()
+    layer.marks = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        layer(x, logits)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kern = {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in layer.marks.items()}
+    layer.marks = None
+    log(f"{ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+    work = gemm_work(wl, layer, torch)
+    dtype = "fp8_e4m3" if wl.fp8 else "bf16"
+    roof = roofline(work["w13_flops"], work["w13_bytes"], kern["gemm_w13"], dtype)
+    roof["kernel"] = "grouped_gemm w13 (gate/up)"
+    w2_roof = roofline(work["w2_flops"], work["w2_bytes"], kern["gemm_w2"], dtype)
+    gemm_ms = kern["gemm_w13"] + kern["gemm_w2"]
+    gemm_tflops = (work["w13_flops"] + work["w2_flops"]) / (gemm_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) expert weights)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
+                   "E_local": wl.El, "top_k": wl.k, "layout": layer.layout, "block_e": wl.block_e,
+                   "rows": layer.rows, "assignments": work["assignments"]},
+        "roofline": roof,
+        "gemm": {"tflops_both": round(gemm_tflops, 1),
+                 "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),
+                 "w2": w2_roof},
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or (24 if wl.H * wl.I * wl.k > 2e7 else 64)
+        n_tok = min(n_tok, wl.T)
+        log(f"cpu baseline: oracle on {n_tok} tokens")
+        res["cpu_baseline"] = cpu_baseline(wl, x, logits, n_tok, torch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,11 @@ def build(verbose: bool = False) -> str:
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every kernel's host launch stub must be defined in the library
+    nm = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "_ZN3moe" in l]
+    if missing:
+        raise RuntimeError(f"libmoe has undefined library symbols: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

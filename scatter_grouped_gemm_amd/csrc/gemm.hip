@@ -53,22 +53,36 @@ struct GemmArgs {
   int group_m;
 };
 
-constexpr int kLdsRow = 144;  // bytes per staged row (128 + 16 padding)
+// chunk permutation of LDS stage row r (see the kernel's staging comment)
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN>
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kMaxFp8K = 8192;  // FP8 scale staging in LDS covers K up to this
+
+// LDS bytes: three k-stages (plus, for FP8, the tile's scales) or the bf16 C
+// tile of the epilogue, whichever is larger.
+template <int BM, int BN, bool FP8>
 constexpr int gemm_lds_bytes() {
-  return 2 * (BM + BN) * kLdsRow > BM * (BN * 2 + 16) ? 2 * (BM + BN) * kLdsRow : BM * (BN * 2 + 16);
+  constexpr int stages = 3 * (BM + BN) * 128 +
+                         (FP8 ? (BM + BN / 128) * (kMaxFp8K / 128) : 0);
+  constexpr int ctile = BM * (BN * 2 + 16);
+  return stages > ctile ? stages : ctile;
 }
 
 template <int BM, int BN, bool FP8, bool MASKED>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_STAGE = BM * kLdsRow;
-  constexpr int STAGE = (BM + BN) * kLdsRow;
-  constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte chunks per thread per stage
   static_assert(BM % 32 == 0 && BN % 128 == 0 && WN <= 128, "tile shape");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_rowok[BM];
@@ -123,62 +137,61 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
   const int64_t rowbytes = static_cast<int64_t>(p.K) * ES;
   const int nk = static_cast<int>(rowbytes / 128);
 
-  // ---- global -> LDS staging ------------------------------------------------------
-  const int chunk = tid & 7, lrow = tid >> 3;  // 8 x 16 B chunks per 128-byte row slice
-  const uint8_t* a_src[A_LD];
-  const uint8_t* b_src[B_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    int64_t r = row0 + lrow + 32 * i;
-    r = r > row_last ? row_last : r;
-    a_src[i] = p.A + r * rowbytes + chunk * 16;
-  }
+  // ---- global -> LDS: direct loads, three stages -----------------------------------
+  // A stage holds 128 bytes of every tile row: rows [0, BM) are A rows, rows
+  // [BM, BM+BN) are B rows, 128 bytes apart, with the 16-byte chunks of row r
+  // permuted by chunk ^ swz(r) so that 16 lanes reading one chunk of 16
+  // consecutive rows hit distinct banks.  Each global_load_lds_dwordx4 moves
+  // 8 rows (64 lanes x 16 bytes) straight into LDS; lane i carries the chunk
+  // that belongs at LDS position i, so the permutation costs nothing.
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * 128;
+  constexpr int NST = 3;
+  constexpr int NLD = ROWS / 32;  // load instructions per wavefront per stage
+  const uint8_t* src[NLD];
   const int64_t brow0 = static_cast<int64_t>(g) * p.N + static_cast<int64_t>(nt) * BN;
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) b_src[i] = p.B + (brow0 + lrow + 32 * i) * rowbytes + chunk * 16;
-
-  u32x4_t ra[A_LD], rb[B_LD];
-#define MOE_GLOAD(kt_)                                                                  \
-  do {                                                                                  \
-    const int64_t off_ = static_cast<int64_t>(kt_) * 128;                               \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] =                            \
-        *reinterpret_cast<const u32x4_t*>(a_src[i] + off_);                             \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) rb[i] =                            \
-        *reinterpret_cast<const u32x4_t*>(b_src[i] + off_);                             \
-  } while (0)
-#define MOE_LSTORE(s_)                                                                  \
-  do {                                                                                  \
-    uint8_t* base_ = smem + (s_) * STAGE + lrow * kLdsRow + chunk * 16;                 \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                                    \
-        *reinterpret_cast<u32x4_t*>(base_ + 32 * i * kLdsRow) = ra[i];                  \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                    \
-        *reinterpret_cast<u32x4_t*>(base_ + A_STAGE + 32 * i * kLdsRow) = rb[i];        \
-  } while (0)
-
-  // ---- FP8 scales -------------------------------------------------------------------
-  // activation scale of the lane's row in each of its TM sub-tiles; weight scale
-  // of the wave's 128-column block (uniform over the wave)
-  const uint8_t* as_src[TM];
-  const uint8_t* ws_src = nullptr;
-  int sa[TM], sa_next[TM], sw = 0, sw_next = 0;
-  if (FP8) {
-    const int KB = p.K / 128;
-    const int64_t gbase = MASKED ? static_cast<int64_t>(g) * KB * p.M - static_cast<int64_t>(g) * p.M : 0;
-#pragma unroll
-    for (int im = 0; im < TM; ++im) {
-      int64_t r = row0 + wm * WM + im * 16 + (lane & 15);
+  for (int j = 0; j < NLD; ++j) {
+    const int R = (wave * NLD + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz(R);
+    if (R < BM) {
+      int64_t r = row0 + R;
       r = r > row_last ? row_last : r;
-      as_src[im] = p.A_scale + gbase + r;
+      src[j] = p.A + r * rowbytes + c * 16;
+    } else {
+      src[j] = p.B + (brow0 + (R - BM)) * rowbytes + c * 16;
     }
-    const int nblk = (nt * BN + wn * WN) / 128;
-    ws_src = p.B_scale + (static_cast<int64_t>(g) * (p.N / 128) + nblk) * KB;
   }
-#define MOE_SLOAD(kt_, dst_, dw_)                                                       \
-  do {                                                                                  \
-    const int64_t so_ = static_cast<int64_t>(kt_) * p.M;                                \
-    _Pragma("unroll") for (int im = 0; im < TM; ++im) dst_[im] = as_src[im][so_];       \
-    dw_ = ws_src[kt_];                                                                  \
+#define MOE_DMA(st_, kt_)                                                                  \
+  do {                                                                                     \
+    const int64_t off_ = static_cast<int64_t>(kt_) * 128;                                  \
+    uint8_t* dst_ = smem + (st_) * STAGE + wave * NLD * 1024;                              \
+    _Pragma("unroll") for (int j = 0; j < NLD; ++j) __builtin_amdgcn_global_load_lds(      \
+        src[j] + off_, (__attribute__((address_space(3))) void*)(dst_ + j * 1024),         \
+        16, 0, 0);                                                                         \
   } while (0)
+
+  // ---- FP8 scales, staged in LDS once per tile ----------------------------------------
+  // s_as[kb][r]: activation scale of tile row r for k block kb;
+  // s_bs[nb][kb]: weight block scale of the tile's 128-column block nb.
+  const int KB = p.K / 128;
+  uint8_t* s_as = smem + NST * STAGE;
+  uint8_t* s_bs = s_as + BM * KB;
+  if (FP8) {
+    for (int i = tid; i < KB * BM; i += 256) {
+      const int kb = i / BM, r = i - kb * BM;
+      int64_t row = row0 + r;
+      row = row > row_last ? row_last : row;
+      const int64_t idx = MASKED ? (static_cast<int64_t>(g) * KB + kb) * p.M + (row - static_cast<int64_t>(g) * p.M)
+                                 : static_cast<int64_t>(kb) * p.M + row;
+      s_as[i] = p.A_scale[idx];
+    }
+    for (int i = tid; i < (BN / 128) * KB; i += 256) {
+      const int nb = i / KB, kb = i - nb * KB;
+      s_bs[i] = p.B_scale[(static_cast<int64_t>(g) * (p.N / 128) + nt * (BN / 128) + nb) * KB + kb];
+    }
+  }
+  const int wblk = (wn * WN) / 128;
 
   f32x4_t acc[TN][TM];
 #pragma unroll
@@ -186,76 +199,78 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
 #pragma unroll
     for (int im = 0; im < TM; ++im) acc[jn][im] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  MOE_GLOAD(0);
-  if (FP8) MOE_SLOAD(0, sa, sw);
-  MOE_LSTORE(0);
-  __syncthreads();
-
   const int frag_row = lane & 15;
   const int frag_k = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) {
-      MOE_GLOAD(kt + 1);
-      if (FP8) MOE_SLOAD(kt + 1, sa_next, sw_next);
-    }
-    const uint8_t* As = smem + s * STAGE;
-    const uint8_t* Bs = As + A_STAGE;
-    if (!FP8) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int koff = ks * 64 + frag_k * 16;
-        bf16x8_t af[TM], bf[TN];
-#pragma unroll
-        for (int im = 0; im < TM; ++im)
-          af[im] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + im * 16 + frag_row) * kLdsRow + koff);
-#pragma unroll
-        for (int jn = 0; jn < TN; ++jn)
-          bf[jn] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WN + jn * 16 + frag_row) * kLdsRow + koff);
-#pragma unroll
-        for (int jn = 0; jn < TN; ++jn)
-#pragma unroll
-          for (int im = 0; im < TM; ++im)
-            acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[jn], af[im], acc[jn][im], 0, 0, 0);
-      }
-    } else {
-      const int koff = frag_k * 32;
-      i32x8_t af[TM], bf[TN];
-#pragma unroll
-      for (int im = 0; im < TM; ++im) {
-        const uint8_t* src = As + (wm * WM + im * 16 + frag_row) * kLdsRow + koff;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
-        af[im] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int jn = 0; jn < TN; ++jn) {
-        const uint8_t* src = Bs + (wn * WN + jn * 16 + frag_row) * kLdsRow + koff;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
-        bf[jn] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
-#pragma unroll
-        for (int im = 0; im < TM; ++im)
-          acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[jn], af[im], acc[jn][im], 0, 0, 0, sw, 0, sa[im]);
-    }
-    if (kt + 1 < nk) {
-      MOE_LSTORE(s ^ 1);
-      if (FP8) {
-#pragma unroll
-        for (int im = 0; im < TM; ++im) sa[im] = sa_next[im];
-        sw = sw_next;
-      }
-    }
-    __syncthreads();
-  }
+  // byte offset of logical chunk c of stage row r
+#define MOE_ROWOFF(r_, c_) ((r_) * 128 + (((c_) ^ lds_swz(r_)) << 4))
+#define MOE_COMPUTE(st_, kt_)                                                                     \
+  do {                                                                                            \
+    const uint8_t* S = smem + (st_) * STAGE;                                                      \
+    if (!FP8) {                                                                                   \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                          \
+        const int c = ks * 4 + frag_k;                                                            \
+        bf16x8_t af[TM], bf[TN];                                                                  \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                       \
+          const int r = wm * WM + im * 16 + frag_row;                                             \
+          af[im] = *reinterpret_cast<const bf16x8_t*>(S + MOE_ROWOFF(r, c));                      \
+        }                                                                                         \
+        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                       \
+          const int r = BM + wn * WN + jn * 16 + frag_row;                                        \
+          bf[jn] = *reinterpret_cast<const bf16x8_t*>(S + MOE_ROWOFF(r, c));                      \
+        }                                                                                         \
+        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                         \
+          _Pragma("unroll") for (int im = 0; im < TM; ++im) acc[jn][im] =                         \
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[jn], af[im], acc[jn][im], 0, 0, 0);      \
+      }                                                                                           \
+    } else {                                                                                      \
+      const int c0 = frag_k * 2;                                                                  \
+      i32x8_t af[TM], bf[TN];                                                                     \
+      int sa[TM];                                                                                 \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                         \
+        const int r = wm * WM + im * 16 + frag_row;                                               \
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0));              \
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0 + 1));          \
+        af[im] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                          \
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                         \
+        sa[im] = s_as[(kt_) * BM + wm * WM + im * 16 + frag_row];                                 \
+      }                                                                                           \
+      const int sw = s_bs[wblk * KB + (kt_)];                                                     \
+      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                         \
+        const int r = BM + wn * WN + jn * 16 + frag_row;                                          \
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0));              \
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0 + 1));          \
+        bf[jn] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                          \
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                         \
+      }                                                                                           \
+      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                           \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) acc[jn][im] =                           \
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[jn], af[im], acc[jn][im], 0, 0,   \
+                                                             0, sw, 0, sa[im]);                   \
+    }                                                                                             \
+  } while (0)
 
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-#undef MOE_SLOAD
+  // Scales and row flags were written with ordinary stores: make them visible
+  // before the first step (this also drains their global loads before the
+  // direct loads start counting).
+  __syncthreads();
+  MOE_DMA(0, 0);
+  if (nk > 1) MOE_DMA(1, 1);
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // the loads of step kt are complete once at most the next step's remain
+    if (kt + 1 < nk) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // step kt visible to all; step kt-1's stage free
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nk) {
+      const int st2 = st + 2 >= NST ? st + 2 - NST : st + 2;
+      MOE_DMA(st2, kt + 2);
+    }
+    MOE_COMPUTE(st, kt);
+    __builtin_amdgcn_sched_barrier(0);
+    st = st + 1 == NST ? 0 : st + 1;
+  }
+  __syncthreads();
+
   // ---- epilogue: accumulators -> bf16 tile in LDS -> row-contiguous stores ----------
   constexpr int CROW = BN * 2 + 16;
   uint8_t* Cs = smem;
@@ -279,11 +294,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
       *reinterpret_cast<u32x4_t*>(Cg + static_cast<int64_t>(rr) * p.N + cc * 8) =
           *reinterpret_cast<const u32x4_t*>(Cs + rr * CROW + cc * 16);
   }
+#endif
 }
 
 template <int BM, int BN, bool FP8, bool MASKED>
 int32_t launch_gemm(GemmArgs a, hipStream_t s) {
-  constexpr int lds = gemm_lds_bytes<BM, BN>();
+  constexpr int lds = gemm_lds_bytes<BM, BN, FP8>();
   auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -321,6 +337,7 @@ static int32_t validate_gemm(int32_t dtype, const void* A, const uint8_t* A_scal
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
   if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
+  if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && K > kMaxFp8K) return MOE_EUNSUPPORTED;
   if (!A || !B || !C) return MOE_EINVAL;
   return MOE_OK;
 }
