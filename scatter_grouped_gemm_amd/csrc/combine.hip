@@ -6,6 +6,7 @@
 
 namespace moe {
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Y,
                                                       int64_t num_rows,
                                                       const int32_t* __restrict__ src2dst,
@@ -22,15 +23,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   for (int col = threadIdx.x * 8; col < H; col += 256 * 8) {
+    // all slot rows are loaded first (independent loads in flight), then
+    // summed strictly in slot order
+    uint4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int r = j < k ? rows[j] : -1;
+      v[j] = r >= 0 ? *reinterpret_cast<const uint4*>(Y + static_cast<int64_t>(r) * H + col)
+                    : make_uint4(0, 0, 0, 0);
+    }
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k || rows[j] < 0) continue;
       const float wj = wt[j];
-      const uint4 v = *reinterpret_cast<const uint4*>(Y + static_cast<int64_t>(r) * H + col);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = __fadd_rn(acc[2 * i], __fmul_rn(wj, bf16_to_f32(static_cast<uint16_t>(u[i] & 0xffffu))));
@@ -55,8 +64,17 @@ extern "C" int32_t moe_combine(const void* Y, int64_t num_rows, const int32_t* s
   if (H % 8 != 0) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!Y || !src2dst || !topk_weights || !out) return MOE_EINVAL;
-  moe::combine_kernel<<<T, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(Y), num_rows, src2dst, topk_weights, k, H, static_cast<uint16_t*>(out));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* y = static_cast<const uint16_t*>(Y);
+  uint16_t* o = static_cast<uint16_t*>(out);
+  if (k <= 2)
+    moe::combine_kernel<2><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+  else if (k <= 4)
+    moe::combine_kernel<4><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+  else if (k <= 8)
+    moe::combine_kernel<8><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+  else
+    moe::combine_kernel<32><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -2,7 +2,10 @@
 // BF16 or FP8 e4m3 with UE8M0 scales, fp32 accumulation, bf16 output.
 //
 // Design (gfx950, wave64, 160 KB LDS):
-//   - One workgroup of 256 threads (4 wavefronts) computes a BM x BN tile of C.
+//   - One workgroup of 512 threads (8 wavefronts, two per SIMD) computes a
+//     BM x BN tile of C; each wavefront owns a 64-row (or BM-row) by 64- or
+//     32-column sub-tile.  The second wavefront on each SIMD issues MFMAs while
+//     the first waits on LDS reads or the per-step barrier.
 //     A k-stage is 128 bytes of every row (64 bf16 or 128 e4m3), staged in LDS
 //     with a 144-byte row pitch (16 bytes of padding keep the 16-lane fragment
 //     reads on distinct banks); two stages are double-buffered: the next
@@ -28,6 +31,8 @@
 //   - Batch invariance: the instruction shape and the k order are the same for
 //     every tile size and layout; a row's result depends only on its own A row
 //     and its expert's weights.
+#include <type_traits>
+
 #include "common.cuh"
 
 namespace moe {
@@ -56,14 +61,16 @@ struct GemmArgs {
 // chunk permutation of LDS stage row r (see the kernel's staging comment)
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+// vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0)
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+constexpr int kWaves = 8;             // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
 constexpr int kMaxFp8K = 8192;  // FP8 scale staging in LDS covers K up to this
 
 // LDS bytes: three k-stages (plus, for FP8, the tile's scales) or the bf16 C
@@ -77,13 +84,15 @@ constexpr int gemm_lds_bytes() {
 }
 
 template <int BM, int BN, bool FP8, bool MASKED>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES_N = kWaves / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
-  static_assert(BM % 32 == 0 && BN % 128 == 0 && WN <= 128, "tile shape");
+  static_assert(BM % 64 == 0 && BN % 128 == 0 && WN <= 128 && WM % 16 == 0 && WN % 16 == 0,
+                "tile shape");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_rowok[BM];
 
@@ -147,9 +156,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
   constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * 128;
   constexpr int NST = 3;
-  constexpr int NLD = ROWS / 32;  // load instructions per wavefront per stage
-  const uint8_t* src[NLD];
+  constexpr int NLD = ROWS / (8 * kWaves);  // load instructions per wavefront per stage
+  static_assert(ROWS % (8 * kWaves) == 0, "stage rows split evenly over the wavefronts");
+  // per-lane source offsets (32-bit) from the A and B tile bases
   const int64_t brow0 = static_cast<int64_t>(g) * p.N + static_cast<int64_t>(nt) * BN;
+  const uint8_t* const a_base = p.A + row0 * rowbytes;
+  const uint8_t* const b_base = p.B + brow0 * rowbytes;
+  uint32_t soff[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
     const int R = (wave * NLD + j) * 8 + (lane >> 3);
@@ -157,18 +170,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
     if (R < BM) {
       int64_t r = row0 + R;
       r = r > row_last ? row_last : r;
-      src[j] = p.A + r * rowbytes + c * 16;
+      soff[j] = static_cast<uint32_t>((r - row0) * rowbytes + c * 16);
     } else {
-      src[j] = p.B + (brow0 + (R - BM)) * rowbytes + c * 16;
+      soff[j] = static_cast<uint32_t>((R - BM) * rowbytes + c * 16);
     }
   }
 #define MOE_DMA(st_, kt_)                                                                  \
   do {                                                                                     \
     const int64_t off_ = static_cast<int64_t>(kt_) * 128;                                  \
+    const uint8_t* ab_ = a_base + off_;                                                    \
+    const uint8_t* bb_ = b_base + off_;                                                    \
     uint8_t* dst_ = smem + (st_) * STAGE + wave * NLD * 1024;                              \
-    _Pragma("unroll") for (int j = 0; j < NLD; ++j) __builtin_amdgcn_global_load_lds(      \
-        src[j] + off_, (__attribute__((address_space(3))) void*)(dst_ + j * 1024),         \
-        16, 0, 0);                                                                         \
+    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                      \
+      const bool is_a_ = (wave * NLD + j) * 8 < BM;                                        \
+      __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                      \
+          (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);           \
+    }                                                                                      \
   } while (0)
 
   // ---- FP8 scales, staged in LDS once per tile ----------------------------------------
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
   uint8_t* s_as = smem + NST * STAGE;
   uint8_t* s_bs = s_as + BM * KB;
   if (FP8) {
-    for (int i = tid; i < KB * BM; i += 256) {
+    for (int i = tid; i < KB * BM; i += kThreads) {
       const int kb = i / BM, r = i - kb * BM;
       int64_t row = row0 + r;
       row = row > row_last ? row_last : row;
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
                                  : static_cast<int64_t>(kb) * p.M + row;
       s_as[i] = p.A_scale[idx];
     }
-    for (int i = tid; i < (BN / 128) * KB; i += 256) {
+    for (int i = tid; i < (BN / 128) * KB; i += kThreads) {
       const int nb = i / KB, kb = i - nb * KB;
       s_bs[i] = p.B_scale[(static_cast<int64_t>(g) * (p.N / 128) + nt * (BN / 128) + nb) * KB + kb];
     }
@@ -201,52 +218,89 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
 
   const int frag_row = lane & 15;
   const int frag_k = lane >> 4;
-  // byte offset of logical chunk c of stage row r
-#define MOE_ROWOFF(r_, c_) ((r_) * 128 + (((c_) ^ lds_swz(r_)) << 4))
-#define MOE_COMPUTE(st_, kt_)                                                                     \
-  do {                                                                                            \
-    const uint8_t* S = smem + (st_) * STAGE;                                                      \
-    if (!FP8) {                                                                                   \
-      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                          \
-        const int c = ks * 4 + frag_k;                                                            \
-        bf16x8_t af[TM], bf[TN];                                                                  \
-        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                       \
-          const int r = wm * WM + im * 16 + frag_row;                                             \
-          af[im] = *reinterpret_cast<const bf16x8_t*>(S + MOE_ROWOFF(r, c));                      \
-        }                                                                                         \
-        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                       \
-          const int r = BM + wn * WN + jn * 16 + frag_row;                                        \
-          bf[jn] = *reinterpret_cast<const bf16x8_t*>(S + MOE_ROWOFF(r, c));                      \
-        }                                                                                         \
-        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                         \
-          _Pragma("unroll") for (int im = 0; im < TM; ++im) acc[jn][im] =                         \
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[jn], af[im], acc[jn][im], 0, 0, 0);      \
-      }                                                                                           \
-    } else {                                                                                      \
-      const int c0 = frag_k * 2;                                                                  \
-      i32x8_t af[TM], bf[TN];                                                                     \
-      int sa[TM];                                                                                 \
-      _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                         \
-        const int r = wm * WM + im * 16 + frag_row;                                               \
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0));              \
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0 + 1));          \
-        af[im] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                          \
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                         \
-        sa[im] = s_as[(kt_) * BM + wm * WM + im * 16 + frag_row];                                 \
-      }                                                                                           \
-      const int sw = s_bs[wblk * KB + (kt_)];                                                     \
-      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                         \
-        const int r = BM + wn * WN + jn * 16 + frag_row;                                          \
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0));              \
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(S + MOE_ROWOFF(r, c0 + 1));          \
-        bf[jn] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                          \
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                         \
-      }                                                                                           \
-      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                           \
-        _Pragma("unroll") for (int im = 0; im < TM; ++im) acc[jn][im] =                           \
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[jn], af[im], acc[jn][im], 0, 0,   \
-                                                             0, sw, 0, sa[im]);                   \
-    }                                                                                             \
+  // Fragment rows are (multiple of 16) + frag_row, so the chunk permutation
+  // depends on the lane only: the byte offset of logical chunk c of the lane's
+  // row in the sub-tile starting at stage row rb is rb*128 + frag_row*128 +
+  // ((c ^ swz_l) << 4).
+  const int swz_l = lds_swz(frag_row);
+#define MOE_ROWOFF(rb_, c_) ((rb_) * 128 + frag_row * 128 + (((c_) ^ swz_l) << 4))
+
+  // ---- fragments, software-pipelined one k-step ahead ------------------------------
+  // Each step: wait for the next stage and for this wave's pending LDS reads,
+  // barrier, refill the stage just consumed (k+3), issue the LDS reads of step
+  // k+1 into the spare fragment set, then run step k's MFMAs from registers.
+  // The reads of step k+1 thus overlap the MFMAs of step k.
+  using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
+  constexpr int KS = FP8 ? 1 : 2;  // MFMA k-substeps per 128-byte stage
+  struct Frags {
+    frag_t a[KS][TM];
+    frag_t b[KS][TN];
+    int sa[TM];
+    int sw;
+  };
+#define MOE_LOAD(F_, st_, kt_)                                                                   \
+  do {                                                                                           \
+    const uint8_t* S_ = smem + (st_) * STAGE;                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                        \
+        const int rb_ = wm * WM + im * 16;                                                       \
+        if constexpr (FP8) {                                                                     \
+          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2));     \
+          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2 + 1)); \
+          F_.a[ks][im] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
+                                 (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
+        } else {                                                                                 \
+          F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+        }                                                                                        \
+      }                                                                                          \
+      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                        \
+        const int rb_ = BM + wn * WN + jn * 16;                                                  \
+        if constexpr (FP8) {                                                                     \
+          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2));     \
+          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2 + 1)); \
+          F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
+                                 (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
+        } else {                                                                                 \
+          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+    if constexpr (FP8) {                                                                         \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im)                                          \
+        F_.sa[im] = s_as[(kt_) * BM + wm * WM + im * 16 + frag_row];                             \
+      F_.sw = s_bs[wblk * KB + (kt_)];                                                           \
+    }                                                                                            \
+  } while (0)
+#define MOE_MMA(F_)                                                                              \
+  do {                                                                                           \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                            \
+      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                          \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
+          if constexpr (FP8)                                                                     \
+            acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                      \
+                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], 0, 0, 0, F_.sw, 0, F_.sa[im]);          \
+          else                                                                                   \
+            acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F_.b[ks][jn], F_.a[ks][im],    \
+                                                                  acc[jn][im], 0, 0, 0);         \
+        }                                                                                        \
+  } while (0)
+  // step k: FC_ holds step k's fragments, FN_ receives step k+1's.  The body
+  // has no branches: near the end the refill re-reads the last k-step into a
+  // stage that is never read again and the final fragment load reads a stale
+  // stage, so every step issues the same number of direct loads and the wait
+  // count is the same constant everywhere.
+#define MOE_STEP(FC_, FN_, k_)                                                                   \
+  do {                                                                                           \
+    wait_vm_lgkm0<NLD>();   /* stage k+1 landed (k+2 may be in flight); reads done */            \
+    __builtin_amdgcn_s_barrier();                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MOE_DMA(st, ((k_) + 3 < nk ? (k_) + 3 : nk - 1));                                            \
+    const int st1_ = st + 1 == NST ? 0 : st + 1;                                                 \
+    MOE_LOAD(FN_, st1_, ((k_) + 1 < nk ? (k_) + 1 : (k_)));                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MOE_MMA(FC_);                                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    st = st1_;                                                                                   \
   } while (0)
 
   // Scales and row flags were written with ordinary stores: make them visible
@@ -254,21 +308,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
   // direct loads start counting).
   __syncthreads();
   MOE_DMA(0, 0);
-  if (nk > 1) MOE_DMA(1, 1);
-  int st = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // the loads of step kt are complete once at most the next step's remain
-    if (kt + 1 < nk) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // step kt visible to all; step kt-1's stage free
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nk) {
-      const int st2 = st + 2 >= NST ? st + 2 - NST : st + 2;
-      MOE_DMA(st2, kt + 2);
-    }
-    MOE_COMPUTE(st, kt);
-    __builtin_amdgcn_sched_barrier(0);
-    st = st + 1 == NST ? 0 : st + 1;
+  MOE_DMA(1, (1 < nk ? 1 : nk - 1));
+  MOE_DMA(2, (2 < nk ? 2 : nk - 1));
+  wait_vm_lgkm0<2 * NLD>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frags f0, f1;
+  MOE_LOAD(f0, 0, 0);
+  int st = 0;  // stage holding step k (read into registers during step k-1)
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    MOE_STEP(f0, f1, kt);
+    MOE_STEP(f1, f0, kt + 1);
   }
+  if (kt < nk) MOE_STEP(f0, f1, kt);
+  wait_vm_lgkm0<0>();
+#undef MOE_DMA
+#undef MOE_ROWOFF
+#undef MOE_LOAD
+#undef MOE_MMA
+#undef MOE_STEP
   __syncthreads();
 
   // ---- epilogue: accumulators -> bf16 tile in LDS -> row-contiguous stores ----------
@@ -288,12 +347,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const GemmArgs p) 
   __syncthreads();
   constexpr int CPR = BN / 8;  // 16-byte chunks per output row
   uint16_t* Cg = p.C + row0 * p.N + static_cast<int64_t>(nt) * BN;
-  for (int idx = tid; idx < BM * CPR; idx += 256) {
+  for (int idx = tid; idx < BM * CPR; idx += kThreads) {
     const int rr = idx / CPR, cc = idx - rr * CPR;
     if (s_rowok[rr])
       *reinterpret_cast<u32x4_t*>(Cg + static_cast<int64_t>(rr) * p.N + cc * 8) =
           *reinterpret_cast<const u32x4_t*>(Cs + rr * CROW + cc * 16);
   }
+#endif
 #endif
 }
 
@@ -320,7 +380,7 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (grid == 0) return MOE_OK;
   if (grid >= (1ll << 31)) return MOE_EINVAL;
   if (a.group_m <= 0) a.group_m = 8;
-  kern<<<static_cast<int>(grid), 256, lds, s>>>(a);
+  kern<<<static_cast<int>(grid), kThreads, lds, s>>>(a);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -393,11 +453,7 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   const bool n256 = N % 256 == 0;
-  // tile height from the hint: small expected counts waste less work on 32 rows
-  if (expected_m > 0 && expected_m <= 32) {
-    if (n256) return fp8 ? launch_gemm<32, 256, true, true>(a, s) : launch_gemm<32, 256, false, true>(a, s);
-    return fp8 ? launch_gemm<32, 128, true, true>(a, s) : launch_gemm<32, 128, false, true>(a, s);
-  }
+  // tile height from the hint: small expected counts waste less work on 64 rows
   if (expected_m > 0 && expected_m <= 64) {
     if (n256) return fp8 ? launch_gemm<64, 256, true, true>(a, s) : launch_gemm<64, 256, false, true>(a, s);
     return fp8 ? launch_gemm<64, 128, true, true>(a, s) : launch_gemm<64, 128, false, true>(a, s);
