@@ -120,25 +120,42 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
     if (rr >= masked_m[g]) return;
   }
   const uint16_t* row = gu + r * 2 * static_cast<int64_t>(I);
-  for (int col = lane * 8; col < I; col += 512) {
-    float gt[8], up[8], a[8];
-    unpack8(*reinterpret_cast<const uint4*>(row + col), gt);
-    unpack8(*reinterpret_cast<const uint4*>(row + I + col), up);
+  // four 512-column passes per round: all loads of a round are issued before
+  // any arithmetic so eight 16-byte loads per lane are in flight
+  constexpr int U = 4;
+  for (int c0 = lane * 8; c0 < I; c0 += U * 512) {
+    uint4 gv[U], uv[U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = gt[i] / (1.0f + expf(-gt[i]));
-      a[i] = bf16_to_f32(f32_to_bf16(s * up[i]));  // the bf16 activation
+    for (int u = 0; u < U; ++u) {
+      const int col = c0 + u * 512;
+      if (col < I) {
+        gv[u] = *reinterpret_cast<const uint4*>(row + col);
+        uv[u] = *reinterpret_cast<const uint4*>(row + I + col);
+      }
     }
-    if (!FP8) {
-      *reinterpret_cast<uint4*>(out + (r * I + col) * 2) = pack8(a);
-    } else {
-      int e;
-      const uint2 qq = quant8_group16(a, &e);
-      *reinterpret_cast<uint2*>(out + r * I + col) = qq;
-      if ((lane & 15) == 0) {
-        const int b = col / 128;
-        const int64_t si = masked_m ? (g * (I / 128) + b) * max_m + rr : static_cast<int64_t>(b) * M + r;
-        out_scale[si] = static_cast<uint8_t>(e + 127);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int col = c0 + u * 512;
+      if (col >= I) break;
+      float gt[8], up[8], a[8];
+      unpack8(gv[u], gt);
+      unpack8(uv[u], up);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sv = gt[i] / (1.0f + expf(-gt[i]));
+        a[i] = bf16_to_f32(f32_to_bf16(sv * up[i]));  // the bf16 activation
+      }
+      if (!FP8) {
+        *reinterpret_cast<uint4*>(out + (r * I + col) * 2) = pack8(a);
+      } else {
+        int e;
+        const uint2 qq = quant8_group16(a, &e);
+        *reinterpret_cast<uint2*>(out + r * I + col) = qq;
+        if ((lane & 15) == 0) {
+          const int b = col / 128;
+          const int64_t si = masked_m ? (g * (I / 128) + b) * max_m + rr : static_cast<int64_t>(b) * M + r;
+          out_scale[si] = static_cast<uint8_t>(e + 127);
+        }
       }
     }
   }

@@ -206,37 +206,50 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
   __syncthreads();
   const uint16_t* xt = x + static_cast<int64_t>(t) * H;
   const int HB = H / 128;
-  for (int col = threadIdx.x * 8; col < H; col += 256 * 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xt + col);
-    if (!FP8) {
-      for (int j = 0; j < k; ++j) {
-        const int r = rows[j];
-        if (r >= 0) *reinterpret_cast<uint4*>(x_out + (static_cast<int64_t>(r) * H + col) * 2) = v;
-      }
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      float f[8];
-      float amax = 0.0f;
+  // up to four 2048-column passes per round, loads issued first
+  constexpr int U = 4;
+  for (int c0 = threadIdx.x * 8; c0 < H; c0 += U * 2048) {
+    uint4 vv[U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
-        f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
-        amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
-      }
-      amax = group_max<16>(amax);
-      const int e = ue8m0_exponent(amax);
-      uint32_t lo = 0, hi = 0;
+    for (int u = 0; u < U; ++u) {
+      const int col = c0 + u * 2048;
+      if (col < H) vv[u] = *reinterpret_cast<const uint4*>(xt + col);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
+    for (int u = 0; u < U; ++u) {
+      const int col = c0 + u * 2048;
+      if (col >= H) break;
+      const uint4 v = vv[u];
+      if (!FP8) {
+        for (int j = 0; j < k; ++j) {
+          const int r = rows[j];
+          if (r >= 0) *reinterpret_cast<uint4*>(x_out + (static_cast<int64_t>(r) * H + col) * 2) = v;
+        }
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+        float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
-      const uint2 q = make_uint2(lo, hi);
-      const bool leader = (threadIdx.x & 15) == 0;
-      for (int j = 0; j < k; ++j) {
-        const int r = rows[j];
-        if (r < 0) continue;
-        *reinterpret_cast<uint2*>(x_out + static_cast<int64_t>(r) * H + col) = q;
-        if (leader) scale_out[scale_index(r, col / 128, scale_ld, max_m, HB)] = static_cast<uint8_t>(e + 127);
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+          f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+          amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+        }
+        amax = group_max<16>(amax);
+        const int e = ue8m0_exponent(amax);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+        const uint2 q = make_uint2(lo, hi);
+        const bool leader = (threadIdx.x & 15) == 0;
+        for (int j = 0; j < k; ++j) {
+          const int r = rows[j];
+          if (r < 0) continue;
+          *reinterpret_cast<uint2*>(x_out + static_cast<int64_t>(r) * H + col) = q;
+          if (leader) scale_out[scale_index(r, col / 128, scale_ld, max_m, HB)] = static_cast<uint8_t>(e + 127);
+        }
       }
     }
   }
