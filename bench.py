@@ -35,8 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fp8_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = default)")
-    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the timed oracle run on the host")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -97,10 +97,11 @@ def roofline(flops, nbytes, ms, dtype):
                 arithmetic_intensity=round(ai, 1))
 
 
-def cpu_baseline(wl, x, logits, n_tok, torch):
-    """The oracle, as it stands, on the first n_tok tokens of the same batch:
-    routing plus the layout-free per-token expert path (w13 -> SiLU-mul ->
-    (requant) -> w2 -> weighted sum), timed on the host cores.  Weight
+def cpu_baseline(wl, x, logits, target_s, torch):
+    """The oracle, as it stands, on a prefix of the same batch: routing plus the
+    layout-free per-token expert path (w13 -> SiLU-mul -> (requant) -> w2 ->
+    weighted sum), timed on the host cores.  A first run on a few tokens sizes
+    the sample so that the timed run takes about target_s seconds.  Weight
     preparation (copying the needed experts' bf16 weights and, for FP8, the
     oracle's own 128x128 block quantisation) is not timed, as it is not part of
     a step on the GPU either."""
@@ -109,38 +110,55 @@ def cpu_baseline(wl, x, logits, n_tok, torch):
     import oracle
     from scatter_grouped_gemm_amd import inputs
     oracle.build(force=False)
-    xs = inputs.bf16_bits(x[:n_tok])
-    ls = logits[:n_tok].cpu().numpy()
-    ids, w = oracle.route_topk(ls, wl.k)
-    local = ids - wl.expert_start
-    need = sorted({int(e) for e in local.reshape(-1) if 0 <= e < wl.El})
-    remap = {e: i for i, e in enumerate(need)}
-    t0 = time.time()
-    w13s, w2s = [], []
-    for e in need:
-        a, b = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
-        a, b = inputs.bf16_bits(a)[None], inputs.bf16_bits(b)[None]
-        if wl.fp8:
-            a, b = oracle.quant_weight_blocks(a), oracle.quant_weight_blocks(b)
-        w13s.append(a)
-        w2s.append(b)
-    log(f"oracle weights for {len(need)} experts prepared in {time.time() - t0:.1f}s")
-    ids_c = np.where((local >= 0) & (local < wl.El),
-                     np.vectorize(lambda e: remap.get(int(e), -1))(local), -1).astype(np.int32)
-    if wl.fp8:
-        W = dict(w13q=np.concatenate([a[0] for a in w13s]), w13s=np.concatenate([a[1] for a in w13s]),
-                 w2q=np.concatenate([a[0] for a in w2s]), w2s=np.concatenate([a[1] for a in w2s]))
-    else:
-        W = dict(w13=np.concatenate(w13s), w2=np.concatenate(w2s))
-    t0 = time.perf_counter()
-    ids2, w2_ = oracle.route_topk(ls, wl.k)
-    out = oracle.moe_dense(xs, ids_c, w2_, 0, len(need), wl.fp8, **W)
-    dt = time.perf_counter() - t0
-    assert np.array_equal(ids2, ids) and out.shape == (n_tok, wl.H)
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return dict(value=round(n_tok / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"first {n_tok} tokens of the batch: routing + per-token expert path "
-                       f"({len(need)} experts), {dt:.1f}s on {cores} threads")
+    cache = {}
+
+    def prepare(local):
+        t0 = time.time()
+        need = sorted({int(e) for e in local.reshape(-1) if 0 <= e < wl.El})
+        for e in need:
+            if e not in cache:
+                a, b = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
+                a, b = inputs.bf16_bits(a)[None], inputs.bf16_bits(b)[None]
+                if wl.fp8:
+                    a, b = oracle.quant_weight_blocks(a), oracle.quant_weight_blocks(b)
+                cache[e] = (a, b)
+        log(f"oracle weights for {len(need)} experts ready ({time.time() - t0:.1f}s)")
+        return need
+
+    def run(n_tok):
+        xs = inputs.bf16_bits(x[:n_tok])
+        ls = logits[:n_tok].cpu().numpy()
+        ids, _ = oracle.route_topk(ls, wl.k)
+        local = ids - wl.expert_start
+        need = prepare(local)
+        remap = np.full(wl.El, -1, np.int32)
+        remap[need] = np.arange(len(need), dtype=np.int32)
+        inside = (local >= 0) & (local < wl.El)
+        ids_c = np.where(inside, remap[np.clip(local, 0, wl.El - 1)], -1).astype(np.int32)
+        if wl.fp8:
+            W = dict(w13q=np.concatenate([cache[e][0][0] for e in need]),
+                     w13s=np.concatenate([cache[e][0][1] for e in need]),
+                     w2q=np.concatenate([cache[e][1][0] for e in need]),
+                     w2s=np.concatenate([cache[e][1][1] for e in need]))
+        else:
+            W = dict(w13=np.concatenate([cache[e][0] for e in need]),
+                     w2=np.concatenate([cache[e][1] for e in need]))
+        t0 = time.perf_counter()
+        ids2, w2_ = oracle.route_topk(ls, wl.k)
+        out = oracle.moe_dense(xs, ids_c, w2_, 0, len(need), wl.fp8, **W)
+        dt = time.perf_counter() - t0
+        assert np.array_equal(ids2, ids) and out.shape == (n_tok, wl.H)
+        return dt, len(need)
+
+    n0 = min(wl.T, 2 * cores)
+    dt0, n_exp0 = run(n0)
+    n = min(wl.T, max(n0, int(n0 * target_s / max(dt0, 1e-6))))
+    log(f"cpu baseline: {n0} tokens took {dt0:.2f}s; timing {n} tokens")
+    dt, n_exp = run(n) if n > n0 else (dt0, n_exp0)
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"first {n} of {wl.T} tokens of the batch: routing + per-token expert path "
+                       f"({n_exp} experts), {dt:.1f}s on {cores} threads")
 
 
 def main():
@@ -151,10 +169,8 @@ def main():
         sys.exit(2)
     import torch
 
-    from scatter_grouped_gemm_amd import _lib, inputs
+    from scatter_grouped_gemm_amd import inputs
     wl = inputs.get(args.workload)
-    if args.group_m:
-        _lib.moe_gemm_set_group_m(args.group_m)
     log(f"workload {wl.name}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -213,10 +229,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n_tok = args.cpu_tokens or (24 if wl.H * wl.I * wl.k > 2e7 else 64)
-        n_tok = min(n_tok, wl.T)
-        log(f"cpu baseline: oracle on {n_tok} tokens")
-        res["cpu_baseline"] = cpu_baseline(wl, x, logits, n_tok, torch)
+        res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
     print(json.dumps(res), flush=True)
 
 

@@ -239,14 +239,6 @@ int32_t moe_combine(const void* Y, int64_t num_rows, const int32_t* src2dst,
                     const float* topk_weights, int32_t T, int32_t k, int32_t H, void* out,
                     void* stream);
 
-/* ---------------------------------------------------------------------------
- * Tuning
- * ------------------------------------------------------------------------- */
-
-/* Number of M tiles that sweep the N tiles together in the grouped GEMMs' tile
- * order (default 8).  Changes only the order tiles run in, never a result.
- * Process-wide.  Returns MOE_EINVAL for values < 1. */
-int32_t moe_gemm_set_group_m(int32_t group_m);
 
 #ifdef __cplusplus
 }

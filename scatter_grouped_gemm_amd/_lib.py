@@ -39,7 +39,6 @@ SIGNATURES = {
     "grouped_gemm_masked": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "silu_and_mul": (_I32, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P]),
-    "moe_gemm_set_group_m": (_I32, [_I32]),
 }
 
 
@@ -110,9 +109,6 @@ def moe_get_device_error(ws: torch.Tensor) -> int:
     _check("moe_get_device_error", lib().moe_get_device_error(_ptr(ws), ctypes.byref(out), _stream()))
     return int(out.value)
 
-
-def moe_gemm_set_group_m(group_m: int) -> None:
-    _check("moe_gemm_set_group_m", lib().moe_gemm_set_group_m(group_m))
 
 
 # --- device calls ----------------------------------------------------------------

@@ -6,10 +6,11 @@
 //     BM x BN tile of C; each wavefront owns a 64-row (or BM-row) by 64- or
 //     32-column sub-tile.  The second wavefront on each SIMD issues MFMAs while
 //     the first waits on LDS reads or the per-step barrier.
-//     A k-stage is 128 bytes of every row (64 bf16 or 128 e4m3), staged in LDS
-//     with a 144-byte row pitch (16 bytes of padding keep the 16-lane fragment
-//     reads on distinct banks); two stages are double-buffered: the next
-//     stage's global loads are in flight while the current one is multiplied.
+//   - A k-step covers 128 bytes of every tile row (64 bf16 or 128 e4m3).  The
+//     rows go from global memory straight into LDS (global_load_lds, 16 bytes
+//     per lane) through three stages: two k-steps are in flight while the
+//     fragments of the next k-step are read from LDS and the current one is
+//     multiplied from registers.
 //   - MFMA: v_mfma_f32_16x16x32_bf16 for BF16 and the block-scaled
 //     v_mfma_scale_f32_16x16x128_f8f6f4 for FP8.  The UE8M0 bytes are exactly
 //     the E8M0 scales that instruction consumes; the per-128-channel activation
@@ -20,14 +21,16 @@
 //     operand, so the accumulator holds C^T: each lane owns 4 consecutive output
 //     columns of one row, which pack into one 8-byte LDS write in the epilogue;
 //     the tile then leaves LDS as 16-byte row-contiguous global stores.
-//   - Tiles never straddle experts: BM divides the 128-row alignment of the
-//     compact layout, so a tile's expert is the expert of its first row, and a
-//     tile whose first row is padding (-1) is skipped without loading anything.
-//     Masked tiles at or past masked_m[g] are skipped the same way.
-//   - Workgroup ids are remapped so that consecutive tiles run on one XCD (the
-//     hardware deals ids round-robin over the 8 XCDs, each with its own L2), and
-//     grouped so `group_m` M-tiles sweep the N-tiles together and share each
-//     weight panel while it is in L2.
+//   - Persistent workgroups, one per CU, walk a tile order built on the device
+//     from the layout: only tiles holding valid rows are listed, each expert's
+//     tiles form one run ordered N-tile-major with its M-tiles innermost, so
+//     the workgroups that run at the same time share each weight panel, and
+//     the list is cut into eight equal contiguous parts, one per XCD (the
+//     hardware deals workgroup ids round-robin over the XCDs, each with its
+//     own L2).  Compact layout: an expert's run is the maximal range of M-tiles
+//     whose first row carries its id (BM divides the 128-row alignment, so a
+//     tile never straddles experts); masked layout: group g has
+//     ceil(masked_m[g] / BM) tiles.
 //   - Batch invariance: the instruction shape and the k order are the same for
 //     every tile size and layout; a row's result depends only on its own A row
 //     and its expert's weights.
@@ -52,11 +55,18 @@ struct GemmArgs {
   const int32_t* rowinfo;  // m_indices (contiguous) or masked_m (masked)
   int64_t M;               // contiguous: rows of A/C; masked: max_m
   int N, K, G;
-  int m_tiles;             // contiguous: all M tiles; masked: M tiles per group
+  int m_tiles;             // contiguous: M tiles of A; masked: M tiles per group
   int n_tiles;
-  int total_m_tiles;       // contiguous: m_tiles; masked: G * m_tiles
-  int group_m;
 };
+
+constexpr int kMaxMaskedGroups = 1024;  // masked tile prefix lives in LDS
+
+// Expert id of the first row of M-tile j, or INT_MIN outside [0, used).
+template <int BM>
+__device__ __forceinline__ int tile_expert(const int32_t* m_indices, int j, int used) {
+  return (j >= 0 && j < used) ? m_indices[static_cast<int64_t>(j) * BM] : INT_MIN;
+}
+
 
 // chunk permutation of LDS stage row r (see the kernel's staging comment)
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -86,7 +96,6 @@ constexpr int gemm_lds_bytes() {
 template <int BM, int BN, bool FP8, bool MASKED>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
   constexpr int WAVES_N = kWaves / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -96,37 +105,124 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_rowok[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid0 = threadIdx.x, lane0 = tid0 & 63, wave0 = tid0 >> 6;
+
+  // ---- tile order (see the file comment) --------------------------------------
+  __shared__ int s_sched[MASKED ? kMaxMaskedGroups + 1 : 8];
+  int used;  // compact: M-tiles up to the last one holding a valid first row
+  if (!MASKED) {
+    int last = -1;
+    for (int j = tid0; j < p.m_tiles; j += kThreads)
+      if (p.rowinfo[static_cast<int64_t>(j) * BM] >= 0) last = j;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
+    if (lane0 == 0) s_sched[wave0] = last;
+    __syncthreads();
+    last = s_sched[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) last = max(last, s_sched[w]);
+    used = __builtin_amdgcn_readfirstlane(last + 1);  // uniform: keep it scalar
+  } else {
+    // s_sched[g] = M-tiles of groups before g (exclusive prefix), s_sched[G] = total
+    constexpr int PER = (kMaxMaskedGroups + kThreads - 1) / kThreads;
+    int cnt[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int g = tid0 * PER + i;
+      int c = 0;
+      if (g < p.G) {
+        int mm = p.rowinfo[g];
+        mm = mm < 0 ? 0 : (mm > p.M ? static_cast<int>(p.M) : mm);
+        c = (mm + BM - 1) / BM;
+      }
+      cnt[i] = c;
+      sum += c;
+    }
+    int incl = sum;  // inclusive scan over the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane0 >= off) incl += v;
+    }
+    __shared__ int s_wsum[kWaves];
+    if (lane0 == 63) s_wsum[wave0] = incl;
+    __syncthreads();
+    int base = incl - sum;
+    for (int w = 0; w < wave0; ++w) base += s_wsum[w];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int g = tid0 * PER + i;
+      if (g < p.G) s_sched[g] = base;
+      base += cnt[i];
+    }
+    if (tid0 == kThreads - 1) s_sched[p.G] = base;  // groups >= G count 0
+    __syncthreads();
+    used = __builtin_amdgcn_readfirstlane(s_sched[p.G]);
+  }
+  // this workgroup's share: XCD x (= blockIdx % 8) takes the x-th eighth of
+  // the order, its workgroups stepping through it side by side
+  const int64_t U = static_cast<int64_t>(used) * p.n_tiles;
+  const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+  const int64_t pos_end = (U * (xcd + 1)) >> 3;
+  for (int64_t pos = ((U * xcd) >> 3) + (blockIdx.x >> 3); pos < pos_end; pos += per_xcd) {
+  // Per-thread indices come from an opaque copy in every iteration, so the
+  // compiler rebuilds per-thread addressing inside the tile instead of keeping
+  // it live (in registers) across the main loop.
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int i0 = static_cast<int>(pos / p.n_tiles);
+  int g, first, run;  // the run of M-tiles [first, first + run) that holds i0
+  if (!MASKED) {
+    // windows of 64 tiles below and above i0, widened until both ends of the
+    // run are found (tiles outside [0, used) compare unequal to any id)
+    const int vb = tile_expert<BM>(p.rowinfo, i0 - 63 + lane, used);
+    const int vf = tile_expert<BM>(p.rowinfo, i0 + 1 + lane, used);
+    g = __builtin_amdgcn_readlane(vb, 63);
+    int lo = i0 - 63;
+    uint64_t d = ballot(vb != g);
+    while (d == 0) {
+      lo -= 64;
+      d = ballot(tile_expert<BM>(p.rowinfo, lo + lane, used) != g);
+    }
+    first = lo + (63 - __builtin_clzll(d)) + 1;
+    int hi = i0 + 1;
+    d = ballot(vf != g);
+    while (d == 0) {
+      hi += 64;
+      d = ballot(tile_expert<BM>(p.rowinfo, hi + lane, used) != g);
+    }
+    run = hi + __builtin_ctzll(d) - first;
+    if (g < 0 || g >= p.G) continue;  // a run of padding tiles
+  } else {
+    int lo = 0, hi = p.G;  // last group whose prefix is <= i0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_sched[mid] <= i0) lo = mid;
+      else hi = mid;
+    }
+    g = __builtin_amdgcn_readfirstlane(lo);
+    first = __builtin_amdgcn_readfirstlane(s_sched[g]);
+    run = __builtin_amdgcn_readfirstlane(s_sched[g + 1]) - first;
+  }
+  const int64_t local = pos - static_cast<int64_t>(first) * p.n_tiles;
+  const int nt = static_cast<int>(local / run);
+  const int mt = first + static_cast<int>(local - static_cast<int64_t>(nt) * run);
 
-  // ---- tile assignment -------------------------------------------------------
-  int pid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int per_group = p.group_m * p.n_tiles;
-  const int grp = pid / per_group;
-  const int first_m = grp * p.group_m;
-  const int gsz = min(p.total_m_tiles - first_m, p.group_m);
-  const int within = pid - grp * per_group;
-  const int mt = first_m + within % gsz;
-  const int nt = within / gsz;
-
-  int g;
   int64_t row0;      // first row of the tile in A / C
   int64_t row_last;  // last addressable row of this group (loads clamp to it)
   int rows_here;     // masked: valid rows from row0
   if (!MASKED) {
     row0 = static_cast<int64_t>(mt) * BM;
-    g = p.rowinfo[row0];
-    if (g < 0 || g >= p.G) return;
     row_last = p.M - 1;
     rows_here = BM;
   } else {
-    g = mt / p.m_tiles;
-    const int r_in0 = (mt - g * p.m_tiles) * BM;
+    const int r_in0 = (mt - first) * BM;
     int mm = p.rowinfo[g];
     mm = mm < 0 ? 0 : (mm > p.M ? static_cast<int>(p.M) : mm);
-    if (r_in0 >= mm) return;
     row0 = static_cast<int64_t>(g) * p.M + r_in0;
     row_last = static_cast<int64_t>(g) * p.M + p.M - 1;
     rows_here = mm - r_in0;
@@ -353,8 +449,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       *reinterpret_cast<u32x4_t*>(Cg + static_cast<int64_t>(rr) * p.N + cc * 8) =
           *reinterpret_cast<const u32x4_t*>(Cs + rr * CROW + cc * 16);
   }
+  __syncthreads();  // the C tile and the row flags are reused by the next tile
+  }  // tile loop
 #endif
-#endif
+}
+
+// Persistent grid: one workgroup per CU (the LDS footprint allows no more),
+// rounded down to a multiple of the 8 XCDs.
+static int persistent_grid() {
+  static int grid[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (grid[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    grid[dev] = cus >= 8 ? cus / 8 * 8 : 8;
+  }
+  return grid[dev];
 }
 
 template <int BM, int BN, bool FP8, bool MASKED>
@@ -369,23 +481,16 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
     attr_set = true;
   }
   a.n_tiles = a.N / BN;
-  if (MASKED) {
-    a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
-    a.total_m_tiles = a.G * a.m_tiles;
-  } else {
-    a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
-    a.total_m_tiles = a.m_tiles;
-  }
-  const int64_t grid = static_cast<int64_t>(a.total_m_tiles) * a.n_tiles;
-  if (grid == 0) return MOE_OK;
-  if (grid >= (1ll << 31)) return MOE_EINVAL;
-  if (a.group_m <= 0) a.group_m = 8;
-  kern<<<static_cast<int>(grid), kThreads, lds, s>>>(a);
+  a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
+  const int64_t tiles = static_cast<int64_t>(MASKED ? a.G : 1) * a.m_tiles * a.n_tiles;
+  if (tiles == 0) return MOE_OK;
+  if (tiles >= (1ll << 40)) return MOE_EINVAL;
+  const int grid = persistent_grid();
+  if (grid == 0) return MOE_EDEVICE;
+  kern<<<grid, kThreads, lds, s>>>(a);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
-
-static int g_group_m = 8;
 
 }  // namespace moe
 
@@ -422,7 +527,6 @@ extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8
   a.N = N;
   a.K = K;
   a.G = G;
-  a.group_m = g_group_m;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   if (N % 256 == 0)
@@ -438,6 +542,7 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   int32_t st = validate_gemm(dtype, A, A_scale, B, B_scale, C, N, K, G);
   if (st != MOE_OK) return st;
   if (!masked_m) return MOE_EINVAL;
+  if (G > kMaxMaskedGroups) return MOE_EUNSUPPORTED;
   GemmArgs a{};
   a.A = static_cast<const uint8_t*>(A);
   a.A_scale = A_scale;
@@ -449,7 +554,6 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   a.N = N;
   a.K = K;
   a.G = G;
-  a.group_m = g_group_m;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   const bool n256 = N % 256 == 0;
@@ -460,11 +564,4 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   }
   if (n256) return fp8 ? launch_gemm<128, 256, true, true>(a, s) : launch_gemm<128, 256, false, true>(a, s);
   return fp8 ? launch_gemm<128, 128, true, true>(a, s) : launch_gemm<128, 128, false, true>(a, s);
-}
-
-// Tuning knob: M-tiles per N sweep in the tile order (does not change results).
-extern "C" int32_t moe_gemm_set_group_m(int32_t group_m) {
-  if (group_m <= 0) return MOE_EINVAL;
-  moe::g_group_m = group_m;
-  return MOE_OK;
 }

@@ -100,7 +100,8 @@ def test_validation_rejects_before_launch():
     assert lib.silu_and_mul(P, 15, 128, None, P, 8, 0, P, None, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 33, 256, P, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 2, 100, P, None) == L.MOE_EUNSUPPORTED
-    assert lib.moe_gemm_set_group_m(0) == L.MOE_EINVAL
+    # masked tile prefix is held on chip for at most 1024 groups
+    assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 8, 64, 256, 256, 1025, None) == L.MOE_EUNSUPPORTED
 
 
 def test_empty_calls_are_no_ops():

@@ -214,9 +214,9 @@ def test_quant_weight_blocks(orc):
 # grouped GEMMs
 # ---------------------------------------------------------------------------
 
-def _gemm_operands(orc, fp8, M_counts, N, K, seed, integer_valued=False):
+def _gemm_operands(orc, fp8, M_counts, N, K, seed, integer_valued=False, block_e=128, extra_rows=128):
     G = len(M_counts)
-    m_idx = compact_layout(M_counts)
+    m_idx = compact_layout(M_counts, block_e, extra_rows)
     M = len(m_idx)
     g = torch.Generator().manual_seed(seed)
     if integer_valued:
@@ -279,6 +279,7 @@ def _check_close(got_bits, ref_bits, valid, tol_rel, fp8=False):
     ([64, 129], 384, 512),
     ([1000, 17, 0, 0, 333], 512, 1024),
     ([0, 0, 1], 128, 128),
+    ([9000, 3, 0, 8300], 128, 128),   # runs of more than 64 M-tiles
 ])
 def test_gemm_contig(orc, fp8, counts, N, K):
     announce("gemm_contig", fp8, counts, N, K)
@@ -288,6 +289,21 @@ def test_gemm_contig(orc, fp8, counts, N, K):
     valid = ops["m_idx"] >= 0
     _check_close(got, ref, valid, 5e-3 if not fp8 else 2e-2, fp8)
     assert np.all(got[~valid] == 0xFFFF)               # padding rows are not written
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_contig_wide_padding(orc, fp8):
+    """Experts padded to 384 rows leave whole M-tiles of padding between
+    experts and 1000 trailing padding rows: those tiles are skipped, every
+    valid row is computed once, integer-valued operands make it exact."""
+    announce("gemm_contig_wide_padding", fp8)
+    ops = _gemm_operands(orc, fp8, [1, 300, 0, 129, 700, 2], 256, 256, seed=5, integer_valued=True,
+                         block_e=384, extra_rows=1000)
+    ref = _ref_gemm(orc, fp8, ops)
+    got = _run_contig(fp8, ops, 256)
+    valid = ops["m_idx"] >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[~valid] == 0xFFFF)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -338,6 +354,35 @@ def test_gemm_masked_all_tile_heights(orc, fp8, integer_valued):
     else:
         _check_close(outs[0], ref, valid, 5e-3 if not fp8 else 2e-2, fp8)
     assert np.all(outs[0][~valid] == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_masked_many_groups(orc, fp8):
+    """700 groups with random counts (a fifth of them empty): the on-chip tile
+    prefix over groups spans every wavefront of the workgroup."""
+    announce("gemm_masked_many_groups", fp8)
+    G, max_m, N, K = 700, 64, 128, 128
+    rng = np.random.default_rng(3)
+    masked = rng.integers(1, max_m + 1, G).astype(np.int32)
+    masked[rng.random(G) < 0.2] = 0
+    ops = _gemm_operands(orc, fp8, [max_m] * G, N, K, seed=13, integer_valued=True)
+    rg = orc.masked_row_group(masked, max_m)
+    A = ops["A"][: G * max_m]
+    C = poison((G, max_m, N), torch.bfloat16)
+    if fp8:
+        ref = orc.gemm_fp8_rows(A, ops["As"][: G * max_m], ops["B"], ops["Bs"], rg)
+        As = ops["As"][: G * max_m].reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
+        L.grouped_gemm_masked(True, u8_dev(A).view(G, max_m, K), u8_dev(As), u8_dev(ops["B"]),
+                              u8_dev(ops["Bs"]), C, i32_dev(masked), 0)
+    else:
+        ref = orc.gemm_bf16_rows(A, ops["B"], rg)
+        L.grouped_gemm_masked(False, to_dev_bf16(A).view(G, max_m, K), None, to_dev_bf16(ops["B"]),
+                              None, C, i32_dev(masked), 0)
+    torch.cuda.synchronize()
+    got = bits(C).reshape(G * max_m, N)
+    valid = rg >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[~valid] == 0xFFFF)
 
 
 # ---------------------------------------------------------------------------
