@@ -97,6 +97,27 @@ def roofline(flops, nbytes, ms, dtype):
                 arithmetic_intensity=round(ai, 1))
 
 
+def measured_traffic(wl_name, which):
+    """HBM bytes per launch of one grouped GEMM (FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain copy's reading) from the rocprofv3 counter summary committed
+    under profiles/, or None when there is none for this workload or the GEMM
+    source has changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"traffic_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    h = hashlib.sha256()
+    for src in ("gemm.hip", "common.cuh"):
+        with open(os.path.join(root, "scatter_grouped_gemm_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    if d.get("gemm_source_sha256") != h.hexdigest() or which not in d:
+        return None
+    return int(d[which]["read_bytes"] + d[which]["write_bytes"])
+
+
 def cpu_baseline(wl, x, logits, target_s, torch):
     """The oracle, as it stands, on a prefix of the same batch: routing plus the
     layout-free per-token expert path (w13 -> SiLU-mul -> (requant) -> w2 ->
@@ -202,7 +223,9 @@ def main():
     dtype = "fp8_e4m3" if wl.fp8 else "bf16"
     roof = roofline(work["w13_flops"], work["w13_bytes"], kern["gemm_w13"], dtype)
     roof["kernel"] = "grouped_gemm w13 (gate/up)"
+    roof["traffic"] = measured_traffic(wl.name, "w13")
     w2_roof = roofline(work["w2_flops"], work["w2_bytes"], kern["gemm_w2"], dtype)
+    w2_roof["traffic"] = measured_traffic(wl.name, "w2")
     gemm_ms = kern["gemm_w13"] + kern["gemm_w2"]
     gemm_tflops = (work["w13_flops"] + work["w2_flops"]) / (gemm_ms * 1e-3) / 1e12
     res = {
