@@ -187,11 +187,14 @@ int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t N, int32_t 
  *   dtype     MOE_DTYPE_BF16 (A bf16 [M][K], B bf16 [G][N][K]; scales NULL) or
  *             MOE_DTYPE_FP8_E4M3_UE8M0 (A e4m3 [M][K] with A_scale [K/128][M],
  *             B e4m3 [G][N][K] with B_scale [G][N/128][K/128])
- *   C         device bf16 [M][N]; rows with m_indices[r] < 0 are not written
+ *   C         device bf16 [M][N].  Rows of an aligned 128-row block whose
+ *             first row is -1 are not written; other rows with m_indices < 0
+ *             (the padding at the end of an expert) receive unspecified values.
  *   m_indices device int32 [M]; layout contract: every aligned 128-row block
  *             holds one expert id on its valid rows, valid rows come first
  *             (what moe_scatter_compact produces with block_e % 128 == 0)
- * Limits: N % 128 == 0, K % 128 == 0, 0 <= m_indices < G.
+ * Limits: N % 128 == 0, K % 128 == 0, K <= 4194304, 0 <= m_indices < G,
+ * ceil(M / 128) <= 8176 (about one million rows) -> else MOE_EUNSUPPORTED.
  * FP8 without scales -> MOE_EUNSUPPORTED (the dtype follows the weights and a
  * contradiction is an error, P3 implementation breakdown item 2). */
 int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale,
@@ -202,9 +205,13 @@ int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale
 /* Masked layout, P2 key source excerpt of _BF16GroupedMaskedWarmupExecutor:
  * C[g, r, :] = A[g, r, :] . B[g]^T for r < masked_m[g].
  *   A [G][max_m][K], C [G][max_m][N]; FP8 A_scale [G][K/128][max_m].
- *   expected_m  a hint of typical masked_m (sizes tiles); it never changes a
- *               result.  0 = no hint.
- * Limits as grouped_gemm_contig. */
+ *   expected_m  a hint of typical masked_m (sizes tiles: 64 rows when
+ *               1 <= expected_m <= 64, else 128); it never changes a result.
+ *               0 = no hint.
+ *   Rows at or past masked_m[g] receive unspecified values, except that rows
+ *   at or past masked_m[g] rounded up to 128 are never written.
+ * Limits: N, K as grouped_gemm_contig; G <= 1024; G * ceil(max_m / tile
+ * height) <= 8176 -> else MOE_EUNSUPPORTED. */
 int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
                             const void* B, const uint8_t* B_scale, void* C,
                             const int32_t* masked_m, int32_t expected_m, int32_t max_m,

@@ -2,38 +2,50 @@
 // BF16 or FP8 e4m3 with UE8M0 scales, fp32 accumulation, bf16 output.
 //
 // Design (gfx950, wave64, 160 KB LDS):
-//   - One workgroup of 512 threads (8 wavefronts, two per SIMD) computes a
-//     BM x BN tile of C; each wavefront owns a 64-row (or BM-row) by 64- or
-//     32-column sub-tile.  The second wavefront on each SIMD issues MFMAs while
-//     the first waits on LDS reads or the per-step barrier.
-//   - A k-step covers 128 bytes of every tile row (64 bf16 or 128 e4m3).  The
-//     rows go from global memory straight into LDS (global_load_lds, 16 bytes
-//     per lane) through three stages: two k-steps are in flight while the
-//     fragments of the next k-step are read from LDS and the current one is
-//     multiplied from registers.
+//   - Persistent workgroups of 512 threads (8 wavefronts, two per SIMD), one
+//     per CU.  A tile of C is BM x BN (128 x 256; 128 x 128 when N % 256 != 0;
+//     masked tiles are 64 rows tall for small expected counts); each
+//     wavefront owns a 64-row (or BM-row) by 64- or 32-column sub-tile.
+//   - The k loop is one flat stream of k-steps over all of the workgroup's
+//     tiles.  A k-step covers 128 bytes of every tile row (64 bf16 or 128
+//     e4m3), moved from global memory straight into LDS (global_load_lds, 16
+//     bytes per lane) through three stages.  The loads run three steps ahead
+//     of the MFMAs and cross into the next tile while the current one
+//     finishes, so a tile costs no pipeline fill or drain.  Each step waits for
+//     its stage with one vmcnt count and one barrier, then reads the next
+//     step's fragments from LDS while the current step's MFMAs run from
+//     registers.  16-byte chunks of each 128-byte LDS row are XOR-permuted so
+//     the 16 lanes of a fragment read hit distinct banks.
 //   - MFMA: v_mfma_f32_16x16x32_bf16 for BF16 and the block-scaled
 //     v_mfma_scale_f32_16x16x128_f8f6f4 for FP8.  The UE8M0 bytes are exactly
 //     the E8M0 scales that instruction consumes; the per-128-channel activation
 //     scale and the 128x128 weight-block scale are both constant over one
 //     128-wide k step, so every lane supplies its row's (column's) byte and no
-//     fp32 rescaling is done in the main loop.
+//     fp32 rescaling is done in the main loop.  The scale bytes of a step ride
+//     with its data: one 1-byte direct load per lane (each lane's byte lands
+//     zero-extended in its own LDS dword) into the stage's scale area.
 //   - The weight tile is the MFMA "A" operand and the activation tile the "B"
 //     operand, so the accumulator holds C^T: each lane owns 4 consecutive output
-//     columns of one row, which pack into one 8-byte LDS write in the epilogue;
-//     the tile then leaves LDS as 16-byte row-contiguous global stores.
-//   - Persistent workgroups, one per CU, walk a tile order built on the device
-//     from the layout: only tiles holding valid rows are listed, each expert's
-//     tiles form one run ordered N-tile-major with its M-tiles innermost, so
-//     the workgroups that run at the same time share each weight panel, and
-//     the list is cut into eight equal contiguous parts, one per XCD (the
-//     hardware deals workgroup ids round-robin over the XCDs, each with its
-//     own L2).  Compact layout: an expert's run is the maximal range of M-tiles
-//     whose first row carries its id (BM divides the 128-row alignment, so a
-//     tile never straddles experts); masked layout: group g has
-//     ceil(masked_m[g] / BM) tiles.
+//     columns of one row and stores them (8 bytes) straight from registers at
+//     the start of the step after the tile's last one, before that step's
+//     loads, so the stores never sit behind a stage the next wait needs.  Rows
+//     past the end of A (compact) or of the group (masked) are not written;
+//     padding rows inside a tile are.
+//   - Tile order, built on the device: only tiles holding valid rows are
+//     listed, each expert's tiles form one run ordered N-tile-major with its
+//     M-tiles innermost, so the workgroups that run at the same time share each
+//     weight panel, and the list is cut into eight equal contiguous parts, one
+//     per XCD (the hardware deals workgroup ids round-robin over the XCDs,
+//     each with its own L2).  Compact layout: a run is a maximal range of
+//     M-tiles whose first rows carry one id (BM divides the 128-row alignment,
+//     so a tile never straddles experts); masked layout: group g has
+//     ceil(masked_m[g] / BM) tiles.  Every workgroup first writes a table of
+//     the runs covering its XCD's share into LDS, so finding a tile's expert
+//     and offsets costs a few LDS reads, never a global load inside the loop.
 //   - Batch invariance: the instruction shape and the k order are the same for
 //     every tile size and layout; a row's result depends only on its own A row
 //     and its expert's weights.
+#include <climits>
 #include <type_traits>
 
 #include "common.cuh"
@@ -59,14 +71,21 @@ struct GemmArgs {
   int n_tiles;
 };
 
-constexpr int kMaxMaskedGroups = 1024;  // masked tile prefix lives in LDS
+constexpr int kWaves = 8;             // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 3;
+constexpr int kScaleArea = kWaves * 256;  // FP8: one 64-dword slot per wavefront per stage
+constexpr int kRunMax = 1024;         // run-table entries: M-tiles of one XCD's share
+constexpr int kMaxMaskedGroups = 1024;
 
-// Expert id of the first row of M-tile j, or INT_MIN outside [0, used).
-template <int BM>
-__device__ __forceinline__ int tile_expert(const int32_t* m_indices, int j, int used) {
-  return (j >= 0 && j < used) ? m_indices[static_cast<int64_t>(j) * BM] : INT_MIN;
+template <int BM, int BN, bool FP8>
+constexpr int gemm_stage_bytes() {
+  return (BM + BN) * 128 + (FP8 ? kScaleArea : 0);
 }
-
+template <int BM, int BN, bool FP8>
+constexpr int gemm_lds_bytes() {
+  return kStages * gemm_stage_bytes<BM, BN, FP8>() + kRunMax * 8;
+}
 
 // chunk permutation of LDS stage row r (see the kernel's staging comment)
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -79,18 +98,82 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-constexpr int kWaves = 8;             // wavefronts per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr int kMaxFp8K = 8192;  // FP8 scale staging in LDS covers K up to this
+// Expert id of the first row of M-tile j (every negative id reads as -1), or
+// INT_MIN outside [0, used), which therefore never equals an id.
+template <int BM>
+__device__ __forceinline__ int tile_expert(const int32_t* m_indices, int j, int used) {
+  if (j < 0 || j >= used) return INT_MIN;
+  const int v = m_indices[static_cast<int64_t>(j) * BM];
+  return v < 0 ? -1 : v;
+}
 
-// LDS bytes: three k-stages (plus, for FP8, the tile's scales) or the bf16 C
-// tile of the epilogue, whichever is larger.
-template <int BM, int BN, bool FP8>
-constexpr int gemm_lds_bytes() {
-  constexpr int stages = 3 * (BM + BN) * 128 +
-                         (FP8 ? (BM + BN / 128) * (kMaxFp8K / 128) : 0);
-  constexpr int ctile = BM * (BN * 2 + 16);
-  return stages > ctile ? stages : ctile;
+// Position pos of the tile order -> expert g, M-tile mt (global index in the
+// order's M-tile space), N-tile nt and the first M-tile of the run.  Table
+// entry j describes M-tile i_lo + j: x = (first - i_lo) | (end - i_lo) << 16
+// as two int16 fields, y = the run's expert id.
+struct TilePos {
+  int g, mt, nt, first;
+};
+// The table is read with a hand-written ds_read: the compiler orders every LDS
+// read it can see after all outstanding direct-to-LDS loads (a full vmcnt
+// drain), but the table never overlaps the stages those loads fill.
+__device__ __forceinline__ int2 read_table(const int2* table, int j) {
+  int2 v;
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const int2*)(table + j)));
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_tiles, int used,
+                                           int pos) {
+  TilePos t;
+  const int i0 = pos / n_tiles;
+  const int2 e = read_table(table, i0 - i_lo);
+  const int x = __builtin_amdgcn_readfirstlane(e.x);
+  t.g = __builtin_amdgcn_readfirstlane(e.y);
+  t.first = i_lo + static_cast<int>(static_cast<int16_t>(x & 0xffff));
+  const int run = i_lo + (x >> 16) - t.first;
+  const int local = pos - t.first * n_tiles;
+  if (run <= 0 || t.first < 0 || t.first + run > used || local < 0 || local >= run * n_tiles) {
+    t.g = -1;  // an inconsistent entry is never used (cannot happen for a well-built table)
+    t.nt = 0;
+    t.mt = 0;
+    return t;
+  }
+  t.nt = local / run;
+  t.mt = t.first + (local - t.nt * run);
+  return t;
+}
+
+// First position at or after pos (stepping by `stride`) whose run is a valid
+// expert, or a position >= end.
+__device__ __forceinline__ int next_tile(const int2* table, int i_lo, int n_tiles, int used, int G,
+                                         int pos, int end, int stride) {
+  for (; pos < end; pos += stride) {
+    const TilePos t = map_pos(table, i_lo, n_tiles, used, pos);
+    if (t.g >= 0 && t.g < G) break;
+  }
+  return pos;
+}
+
+// Rows of the tile at t: first row in A / C, rows that exist (rows past the
+// end of A or of the group are neither loaded nor stored), and the A-scale
+// index of (k block 0, tile row 0); A-scale rows are p.M apart per k block.
+template <int BM, bool MASKED>
+__device__ __forceinline__ void tile_rows(const GemmArgs& p, const TilePos& t, int64_t& row0,
+                                          int& rows, int64_t& as0) {
+  if (!MASKED) {
+    row0 = static_cast<int64_t>(t.mt) * BM;
+    const int64_t left = p.M - row0;
+    rows = left < BM ? static_cast<int>(left) : BM;
+    as0 = row0;
+  } else {
+    const int r_in0 = (t.mt - t.first) * BM;
+    row0 = static_cast<int64_t>(t.g) * p.M + r_in0;
+    const int64_t left = p.M - r_in0;
+    rows = left < BM ? static_cast<int>(left) : BM;
+    as0 = static_cast<int64_t>(t.g) * (p.K / 128) * p.M + r_in0;
+  }
 }
 
 template <int BM, int BN, bool FP8, bool MASKED>
@@ -100,36 +183,50 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   constexpr int WAVES_N = kWaves / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int SDATA = ROWS * 128;                      // stage data bytes
+  constexpr int STAGE = gemm_stage_bytes<BM, BN, FP8>();
+  constexpr int NLD = ROWS / (8 * kWaves);  // 16-byte direct loads per wavefront per stage
+  constexpr int NVM = NLD + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step
+  constexpr int NB = BN / 128;              // weight-scale blocks per tile
+  constexpr int ASW = BM / 64;              // wavefronts fetching activation scales
   static_assert(BM % 64 == 0 && BN % 128 == 0 && WN <= 128 && WM % 16 == 0 && WN % 16 == 0,
                 "tile shape");
+  static_assert(ROWS % (8 * kWaves) == 0, "stage rows split evenly over the wavefronts");
+  static_assert(ASW < kWaves, "a wavefront is left for the weight scales");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_rowok[BM];
+  int2* const table = reinterpret_cast<int2*>(smem + kStages * STAGE);
+  int* const scratch = reinterpret_cast<int*>(smem);  // set-up only (stage memory)
 
-  const int tid0 = threadIdx.x, lane0 = tid0 & 63, wave0 = tid0 >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int n_tiles = p.n_tiles;
 
-  // ---- tile order (see the file comment) --------------------------------------
-  __shared__ int s_sched[MASKED ? kMaxMaskedGroups + 1 : 8];
-  int used;  // compact: M-tiles up to the last one holding a valid first row
+  // ======== set-up: this workgroup's share of the tile order ========
+  int used;  // M-tiles of the order (compact: up to the last valid first row)
   if (!MASKED) {
     int last = -1;
-    for (int j = tid0; j < p.m_tiles; j += kThreads)
+    for (int j = tid; j < p.m_tiles; j += kThreads)
       if (p.rowinfo[static_cast<int64_t>(j) * BM] >= 0) last = j;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
-    if (lane0 == 0) s_sched[wave0] = last;
+    if (lane == 0) scratch[wave] = last;
     __syncthreads();
-    last = s_sched[0];
+    last = scratch[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) last = max(last, s_sched[w]);
-    used = __builtin_amdgcn_readfirstlane(last + 1);  // uniform: keep it scalar
+    for (int w = 1; w < kWaves; ++w) last = max(last, scratch[w]);
+    used = __builtin_amdgcn_readfirstlane(last + 1);
+    __syncthreads();  // scratch is rewritten below
   } else {
-    // s_sched[g] = M-tiles of groups before g (exclusive prefix), s_sched[G] = total
+    // scratch[g] = M-tiles of the groups before g, scratch[G] = total
     constexpr int PER = (kMaxMaskedGroups + kThreads - 1) / kThreads;
+    int* const wsum = scratch + kMaxMaskedGroups + 8;
     int cnt[PER];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int g = tid0 * PER + i;
+      const int g = tid * PER + i;
       int c = 0;
       if (g < p.G) {
         int mm = p.rowinfo[g];
@@ -143,168 +240,205 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int v = __shfl_up(incl, off, 64);
-      if (lane0 >= off) incl += v;
+      if (lane >= off) incl += v;
     }
-    __shared__ int s_wsum[kWaves];
-    if (lane0 == 63) s_wsum[wave0] = incl;
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int base = incl - sum;
-    for (int w = 0; w < wave0; ++w) base += s_wsum[w];
+    for (int w = 0; w < wave; ++w) base += wsum[w];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int g = tid0 * PER + i;
-      if (g < p.G) s_sched[g] = base;
+      const int g = tid * PER + i;
+      if (g < p.G) scratch[g] = base;
       base += cnt[i];
     }
-    if (tid0 == kThreads - 1) s_sched[p.G] = base;  // groups >= G count 0
+    if (tid == kThreads - 1) scratch[p.G] = base;  // groups >= G count 0
     __syncthreads();
-    used = __builtin_amdgcn_readfirstlane(s_sched[p.G]);
+    used = __builtin_amdgcn_readfirstlane(scratch[p.G]);
   }
-  // this workgroup's share: XCD x (= blockIdx % 8) takes the x-th eighth of
-  // the order, its workgroups stepping through it side by side
-  const int64_t U = static_cast<int64_t>(used) * p.n_tiles;
-  const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
-  const int64_t pos_end = (U * (xcd + 1)) >> 3;
-  for (int64_t pos = ((U * xcd) >> 3) + (blockIdx.x >> 3); pos < pos_end; pos += per_xcd) {
-  // Per-thread indices come from an opaque copy in every iteration, so the
-  // compiler rebuilds per-thread addressing inside the tile instead of keeping
-  // it live (in registers) across the main loop.
-  int tid = tid0;
-  asm volatile("" : "+v"(tid));
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int i0 = static_cast<int>(pos / p.n_tiles);
-  int g, first, run;  // the run of M-tiles [first, first + run) that holds i0
-  if (!MASKED) {
-    // windows of 64 tiles below and above i0, widened until both ends of the
-    // run are found (tiles outside [0, used) compare unequal to any id)
-    const int vb = tile_expert<BM>(p.rowinfo, i0 - 63 + lane, used);
-    const int vf = tile_expert<BM>(p.rowinfo, i0 + 1 + lane, used);
-    g = __builtin_amdgcn_readlane(vb, 63);
-    int lo = i0 - 63;
-    uint64_t d = ballot(vb != g);
-    while (d == 0) {
-      lo -= 64;
-      d = ballot(tile_expert<BM>(p.rowinfo, lo + lane, used) != g);
-    }
-    first = lo + (63 - __builtin_clzll(d)) + 1;
-    int hi = i0 + 1;
-    d = ballot(vf != g);
-    while (d == 0) {
-      hi += 64;
-      d = ballot(tile_expert<BM>(p.rowinfo, hi + lane, used) != g);
-    }
-    run = hi + __builtin_ctzll(d) - first;
-    if (g < 0 || g >= p.G) continue;  // a run of padding tiles
-  } else {
-    int lo = 0, hi = p.G;  // last group whose prefix is <= i0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_sched[mid] <= i0) lo = mid;
-      else hi = mid;
-    }
-    g = __builtin_amdgcn_readfirstlane(lo);
-    first = __builtin_amdgcn_readfirstlane(s_sched[g]);
-    run = __builtin_amdgcn_readfirstlane(s_sched[g + 1]) - first;
-  }
-  const int64_t local = pos - static_cast<int64_t>(first) * p.n_tiles;
-  const int nt = static_cast<int>(local / run);
-  const int mt = first + static_cast<int>(local - static_cast<int64_t>(nt) * run);
+  // XCD x (= blockIdx % 8) takes the x-th eighth [lo_x, hi_x) of the order;
+  // its workgroups step through it side by side.
+  const int U = used * n_tiles;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int lo_x = static_cast<int>((static_cast<int64_t>(U) * xcd) >> 3);
+  const int hi_x = static_cast<int>((static_cast<int64_t>(U) * (xcd + 1)) >> 3);
+  if (lo_x + static_cast<int>(blockIdx.x >> 3) >= hi_x) return;
+  const int i_lo = lo_x / n_tiles;
+  const int R = (hi_x - 1) / n_tiles - i_lo + 1;  // <= kRunMax (host bound)
 
-  int64_t row0;      // first row of the tile in A / C
-  int64_t row_last;  // last addressable row of this group (loads clamp to it)
-  int rows_here;     // masked: valid rows from row0
+  // ---- run table for M-tiles [i_lo, i_lo + R) ----
   if (!MASKED) {
-    row0 = static_cast<int64_t>(mt) * BM;
-    row_last = p.M - 1;
-    rows_here = BM;
-  } else {
-    const int r_in0 = (mt - first) * BM;
-    int mm = p.rowinfo[g];
-    mm = mm < 0 ? 0 : (mm > p.M ? static_cast<int>(p.M) : mm);
-    row0 = static_cast<int64_t>(g) * p.M + r_in0;
-    row_last = static_cast<int64_t>(g) * p.M + p.M - 1;
-    rows_here = mm - r_in0;
-  }
-  if (tid < BM) {
-    bool ok;
-    if (!MASKED) {
-      const int64_t r = row0 + tid;
-      ok = r < p.M && p.rowinfo[r] == g;
-    } else {
-      ok = tid < rows_here;
+    int* const ids = scratch + 8;                  // [R]
+    int* const wred = scratch + 8 + kRunMax;       // [2 * kWaves]
+    for (int j = tid; j < R; j += kThreads) ids[j] = tile_expert<BM>(p.rowinfo, i_lo + j, used);
+    if (wave == 0) {
+      // start of the run holding i_lo: windows of 64 tiles below it
+      const int e = tile_expert<BM>(p.rowinfo, i_lo, used);
+      int lo = i_lo - 64;
+      uint64_t d = ballot(tile_expert<BM>(p.rowinfo, lo + lane, used) != e);
+      while (d == 0) {
+        lo -= 64;
+        d = ballot(tile_expert<BM>(p.rowinfo, lo + lane, used) != e);
+      }
+      if (lane == 0) scratch[0] = lo + (63 - __builtin_clzll(d)) + 1;
+    } else if (wave == 1) {
+      // end of the run holding the share's last M-tile
+      const int ih = i_lo + R - 1;
+      const int e = tile_expert<BM>(p.rowinfo, ih, used);
+      int hi = ih + 1;
+      uint64_t d = ballot(tile_expert<BM>(p.rowinfo, hi + lane, used) != e);
+      while (d == 0) {
+        hi += 64;
+        d = ballot(tile_expert<BM>(p.rowinfo, hi + lane, used) != e);
+      }
+      if (lane == 0) scratch[1] = hi + __builtin_ctzll(d);
     }
-    s_rowok[tid] = ok ? 1 : 0;
+    __syncthreads();
+    const int first_lo = scratch[0], end_hi = scratch[1];
+    // entries 2*tid, 2*tid+1: run starts are a prefix maximum of the start
+    // marks, run ends a suffix minimum of the end marks
+    int id[2], v[2], w[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = 2 * tid + q;
+      if (j < R) {
+        id[q] = ids[j];
+        v[q] = j == 0 ? first_lo : (ids[j - 1] != id[q] ? i_lo + j : INT_MIN);
+        w[q] = j == R - 1 ? end_hi : (ids[j + 1] != id[q] ? i_lo + j + 1 : INT_MAX);
+      } else {
+        id[q] = -1;
+        v[q] = INT_MIN;
+        w[q] = INT_MAX;
+      }
+    }
+    int pre = max(v[0], v[1]);
+    int suf = min(w[0], w[1]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(pre, off, 64);
+      const int b = __shfl_down(suf, off, 64);
+      if (lane >= off) pre = max(pre, a);
+      if (lane + off < 64) suf = min(suf, b);
+    }
+    if (lane == 63) wred[wave] = pre;
+    if (lane == 0) wred[kWaves + wave] = suf;
+    __syncthreads();
+    int before = INT_MIN, after = INT_MAX;
+    for (int q = 0; q < wave; ++q) before = max(before, wred[q]);
+    for (int q = wave + 1; q < kWaves; ++q) after = min(after, wred[kWaves + q]);
+    const int pre_x = __shfl_up(pre, 1, 64);
+    const int suf_x = __shfl_down(suf, 1, 64);
+    if (lane > 0) before = max(before, pre_x);
+    if (lane < 63) after = min(after, suf_x);
+    const int f0 = max(before, v[0]), f1 = max(f0, v[1]);
+    const int e1 = min(after, w[1]), e0 = min(e1, w[0]);
+    if (2 * tid < R)
+      table[2 * tid] = make_int2(((f0 - i_lo) & 0xffff) | ((e0 - i_lo) << 16), id[0]);
+    if (2 * tid + 1 < R)
+      table[2 * tid + 1] = make_int2(((f1 - i_lo) & 0xffff) | ((e1 - i_lo) << 16), id[1]);
+  } else {
+    const int* const pre = scratch;
+    for (int j = tid; j < R; j += kThreads) {
+      const int i = i_lo + j;
+      int lo = 0, hi = p.G;  // last group whose prefix is <= i
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      table[j] = make_int2(((pre[lo] - i_lo) & 0xffff) | ((pre[lo + 1] - i_lo) << 16), lo);
+    }
   }
+  __syncthreads();  // table complete; stage memory is free
 
+  // ======== the flat k-step stream ========
   constexpr int ES = FP8 ? 1 : 2;
   const int64_t rowbytes = static_cast<int64_t>(p.K) * ES;
   const int nk = static_cast<int>(rowbytes / 128);
+  const int KB = p.K / 128;
+  const int G = p.G;
 
-  // ---- global -> LDS: direct loads, three stages -----------------------------------
-  // A stage holds 128 bytes of every tile row: rows [0, BM) are A rows, rows
-  // [BM, BM+BN) are B rows, 128 bytes apart, with the 16-byte chunks of row r
-  // permuted by chunk ^ swz(r) so that 16 lanes reading one chunk of 16
-  // consecutive rows hit distinct banks.  Each global_load_lds_dwordx4 moves
-  // 8 rows (64 lanes x 16 bytes) straight into LDS; lane i carries the chunk
-  // that belongs at LDS position i, so the permutation costs nothing.
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * 128;
-  constexpr int NST = 3;
-  constexpr int NLD = ROWS / (8 * kWaves);  // load instructions per wavefront per stage
-  static_assert(ROWS % (8 * kWaves) == 0, "stage rows split evenly over the wavefronts");
-  // per-lane source offsets (32-bit) from the A and B tile bases
-  const int64_t brow0 = static_cast<int64_t>(g) * p.N + static_cast<int64_t>(nt) * BN;
-  const uint8_t* const a_base = p.A + row0 * rowbytes;
-  const uint8_t* const b_base = p.B + brow0 * rowbytes;
-  uint32_t soff[NLD];
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int R = (wave * NLD + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ lds_swz(R);
-    if (R < BM) {
-      int64_t r = row0 + R;
-      r = r > row_last ? row_last : r;
-      soff[j] = static_cast<uint32_t>((r - row0) * rowbytes + c * 16);
-    } else {
-      soff[j] = static_cast<uint32_t>((R - BM) * rowbytes + c * 16);
-    }
-  }
-#define MOE_DMA(st_, kt_)                                                                  \
-  do {                                                                                     \
-    const int64_t off_ = static_cast<int64_t>(kt_) * 128;                                  \
-    const uint8_t* ab_ = a_base + off_;                                                    \
-    const uint8_t* bb_ = b_base + off_;                                                    \
-    uint8_t* dst_ = smem + (st_) * STAGE + wave * NLD * 1024;                              \
-    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                      \
-      const bool is_a_ = (wave * NLD + j) * 8 < BM;                                        \
-      __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                      \
-          (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);           \
-    }                                                                                      \
+  // -- load side: the tile and k-step whose stage is filled next --
+  int d_pos = next_tile(table, i_lo, n_tiles, used, G, lo_x + static_cast<int>(blockIdx.x >> 3),
+                                hi_x, per_xcd);
+  if (d_pos >= hi_x) return;
+  int d_k = 0;
+  int64_t d_aoff, d_boff, d_as0, d_bs0;  // byte offsets of the tile in A and B; scale indices
+  int d_rows;
+  uint32_t soff[NLD];  // per-lane source offsets from the tile's A / B rows
+  // A direct load moves 8 rows (64 lanes x 16 bytes) into LDS; lane i carries
+  // the 16-byte chunk that belongs at LDS position i of its row, i.e. source
+  // chunk (i & 7) ^ swz(row).  Stage rows [0, BM) are A rows, [BM, ROWS) B rows.
+#define MOE_DSET(pos_)                                                                        \
+  do {                                                                                        \
+    const TilePos t_ = map_pos(table, i_lo, n_tiles, used, (pos_));                                 \
+    int64_t r0_;                                                                              \
+    tile_rows<BM, MASKED>(p, t_, r0_, d_rows, d_as0);                                         \
+    d_pos = (pos_);                                                                           \
+    d_aoff = r0_ * rowbytes;                                                                  \
+    d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * BN) * rowbytes; \
+    d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * NB) * KB;                     \
+    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                         \
+      const int R_ = (wave * NLD + j) * 8 + (lane >> 3);                                      \
+      const int c_ = (lane & 7) ^ lds_swz(R_);                                                \
+      const int r_ = R_ < BM ? (R_ < d_rows ? R_ : d_rows - 1) : R_ - BM;                     \
+      soff[j] = static_cast<uint32_t>(r_ * rowbytes + c_ * 16);                               \
+    }                                                                                         \
+  } while (0)
+  MOE_DSET(d_pos);
+
+  // One k-step of loads into stage st_: for FP8 first the scale bytes (wave w
+  // < ASW: activation scales of tile rows 64w..64w+63; wave ASW: the NB
+  // weight-block scales; the rest repeat those), then the data rows.
+#define MOE_ISSUE(st_)                                                                          \
+  do {                                                                                          \
+    uint8_t* const stg_ = smem + (st_) * STAGE;                                                 \
+    if constexpr (FP8) {                                                                        \
+      const uint8_t* src_;                                                                      \
+      if (wave < ASW) {                                                                         \
+        int r_ = wave * 64 + lane;                                                              \
+        r_ = r_ < d_rows ? r_ : d_rows - 1;                                                     \
+        src_ = p.A_scale + d_as0 + static_cast<int64_t>(d_k) * p.M + r_;                       \
+      } else {                                                                                  \
+        const int nb_ = lane < NB ? lane : NB - 1;                                              \
+        src_ = p.B_scale + d_bs0 + static_cast<int64_t>(nb_) * KB + d_k;                        \
+      }                                                                                         \
+      __builtin_amdgcn_global_load_lds(src_,                                                    \
+          (__attribute__((address_space(3))) void*)(stg_ + SDATA + wave * 256), 1, 0, 0);       \
+    }                                                                                           \
+    const uint8_t* ab_ = p.A + d_aoff + static_cast<int64_t>(d_k) * 128;                        \
+    const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * 128;                        \
+    uint8_t* const dst_ = stg_ + wave * NLD * 1024;                                             \
+    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                           \
+      const bool is_a_ = (wave * NLD + j) * 8 < BM;                                             \
+      __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                           \
+          (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);                \
+    }                                                                                           \
+    /* advance; past the last tile keep re-reading its last k-step (never used) */             \
+    if (++d_k == nk) {                                                                          \
+      d_k = 0;                                                                                  \
+      const int np_ = next_tile(table, i_lo, n_tiles, used, G, d_pos + per_xcd, hi_x, per_xcd); \
+      if (np_ < hi_x) MOE_DSET(np_);                                                            \
+      else d_k = nk - 1;                                                                        \
+    }                                                                                           \
   } while (0)
 
-  // ---- FP8 scales, staged in LDS once per tile ----------------------------------------
-  // s_as[kb][r]: activation scale of tile row r for k block kb;
-  // s_bs[nb][kb]: weight block scale of the tile's 128-column block nb.
-  const int KB = p.K / 128;
-  uint8_t* s_as = smem + NST * STAGE;
-  uint8_t* s_bs = s_as + BM * KB;
-  if (FP8) {
-    for (int i = tid; i < KB * BM; i += kThreads) {
-      const int kb = i / BM, r = i - kb * BM;
-      int64_t row = row0 + r;
-      row = row > row_last ? row_last : row;
-      const int64_t idx = MASKED ? (static_cast<int64_t>(g) * KB + kb) * p.M + (row - static_cast<int64_t>(g) * p.M)
-                                 : static_cast<int64_t>(kb) * p.M + row;
-      s_as[i] = p.A_scale[idx];
-    }
-    for (int i = tid; i < (BN / 128) * KB; i += kThreads) {
-      const int nb = i / KB, kb = i - nb * KB;
-      s_bs[i] = p.B_scale[(static_cast<int64_t>(g) * (p.N / 128) + nt * (BN / 128) + nb) * KB + kb];
-    }
-  }
-  const int wblk = (wn * WN) / 128;
+  // -- compute side: the tile being accumulated --
+  int c_k = 0;
+  int c_pos = d_pos;
+  int c_next = next_tile(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);
+  int64_t c_row0;
+  int c_rows, c_nt;
+#define MOE_CSET(pos_)                                                                        \
+  do {                                                                                        \
+    const TilePos t_ = map_pos(table, i_lo, n_tiles, used, (pos_));                                 \
+    int64_t as0_;                                                                             \
+    tile_rows<BM, MASKED>(p, t_, c_row0, c_rows, as0_);                                       \
+    c_nt = t_.nt;                                                                             \
+    c_pos = (pos_);                                                                           \
+  } while (0)
+  MOE_CSET(c_pos);
 
   f32x4_t acc[TN][TM];
 #pragma unroll
@@ -314,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 
   const int frag_row = lane & 15;
   const int frag_k = lane >> 4;
+  const int wblk = (wn * WN) / 128;
   // Fragment rows are (multiple of 16) + frag_row, so the chunk permutation
   // depends on the lane only: the byte offset of logical chunk c of the lane's
   // row in the sub-tile starting at stage row rb is rb*128 + frag_row*128 +
@@ -321,11 +456,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int swz_l = lds_swz(frag_row);
 #define MOE_ROWOFF(rb_, c_) ((rb_) * 128 + frag_row * 128 + (((c_) ^ swz_l) << 4))
 
-  // ---- fragments, software-pipelined one k-step ahead ------------------------------
-  // Each step: wait for the next stage and for this wave's pending LDS reads,
-  // barrier, refill the stage just consumed (k+3), issue the LDS reads of step
-  // k+1 into the spare fragment set, then run step k's MFMAs from registers.
-  // The reads of step k+1 thus overlap the MFMAs of step k.
   using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
   constexpr int KS = FP8 ? 1 : 2;  // MFMA k-substeps per 128-byte stage
   struct Frags {
@@ -334,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     int sa[TM];
     int sw;
   };
-#define MOE_LOAD(F_, st_, kt_)                                                                   \
+#define MOE_LOAD(F_, st_)                                                                        \
   do {                                                                                           \
     const uint8_t* S_ = smem + (st_) * STAGE;                                                    \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
@@ -362,9 +492,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       }                                                                                          \
     }                                                                                            \
     if constexpr (FP8) {                                                                         \
+      const uint8_t* X_ = S_ + SDATA;                                                            \
       _Pragma("unroll") for (int im = 0; im < TM; ++im)                                          \
-        F_.sa[im] = s_as[(kt_) * BM + wm * WM + im * 16 + frag_row];                             \
-      F_.sw = s_bs[wblk * KB + (kt_)];                                                           \
+        F_.sa[im] = X_[(wm * WM + im * 16 + frag_row) * 4];                                      \
+      F_.sw = X_[ASW * 256 + wblk * 4];                                                          \
     }                                                                                            \
   } while (0)
 #define MOE_MMA(F_)                                                                              \
@@ -380,77 +511,88 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
                                                                   acc[jn][im], 0, 0, 0);         \
         }                                                                                        \
   } while (0)
-  // step k: FC_ holds step k's fragments, FN_ receives step k+1's.  The body
-  // has no branches: near the end the refill re-reads the last k-step into a
-  // stage that is never read again and the final fragment load reads a stale
-  // stage, so every step issues the same number of direct loads and the wait
-  // count is the same constant everywhere.
-#define MOE_STEP(FC_, FN_, k_)                                                                   \
+  // Stores of the finished compute tile (lane: 4 consecutive columns of a row
+  // per 16x16 block), then a fresh accumulator.
+#define MOE_EPILOGUE()                                                                           \
   do {                                                                                           \
-    wait_vm_lgkm0<NLD>();   /* stage k+1 landed (k+2 may be in flight); reads done */            \
+    uint16_t* const cg_ = p.C + c_row0 * p.N + static_cast<int64_t>(c_nt) * BN + wn * WN + frag_k * 4; \
+    _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                          \
+      const int r_ = wm * WM + im * 16 + frag_row;                                               \
+      if (r_ < c_rows) {                                                                         \
+        uint16_t* const crow_ = cg_ + static_cast<int64_t>(r_) * p.N;                            \
+        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                      \
+          const f32x4_t v_ = acc[jn][im];                                                        \
+          const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                       \
+                               (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);                \
+          const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                       \
+                               (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);                \
+          *reinterpret_cast<u32x2_t*>(crow_ + jn * 16) = u32x2_t{lo_, hi_};                      \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+    _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                            \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) acc[jn][im] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
+  } while (0)
+  // One step s (FC_ holds its fragments, read during step s-1):
+  //   wait until stage s+1 (and its scales) landed and this wavefront's LDS
+  //   reads are done, barrier; if step s-1 finished a tile, store it and move
+  //   the compute side on; refill the stage step s used with step s+3; read
+  //   step s+1's fragments into FN_; run step s's MFMAs.
+  //   The wait count is the number of vector memory instructions one refill
+  //   issues: those of step s+2 may still be in flight, all older ones (the
+  //   refill of step s+1, the stores) have completed because vector memory
+  //   loads complete in issue order.
+  bool c_epi = false;
+  bool done = false;
+#define MOE_STEP(FC_, FN_)                                                                       \
+  do {                                                                                           \
+    wait_vm_lgkm0<NVM>();                                                                        \
     __builtin_amdgcn_s_barrier();                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    MOE_DMA(st, ((k_) + 3 < nk ? (k_) + 3 : nk - 1));                                            \
-    const int st1_ = st + 1 == NST ? 0 : st + 1;                                                 \
-    MOE_LOAD(FN_, st1_, ((k_) + 1 < nk ? (k_) + 1 : (k_)));                                      \
+    if (c_epi) {                                                                                 \
+      MOE_EPILOGUE();                                                                            \
+      c_epi = false;                                                                             \
+      MOE_CSET(c_next);                                                                          \
+      c_next = next_tile(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);       \
+    }                                                                                            \
+    MOE_ISSUE(st);                                                                               \
+    const int st1_ = st + 1 == kStages ? 0 : st + 1;                                             \
+    MOE_LOAD(FN_, st1_);                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     MOE_MMA(FC_);                                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     st = st1_;                                                                                   \
+    if (++c_k == nk) {                                                                           \
+      c_k = 0;                                                                                   \
+      c_epi = true;                                                                              \
+      done = c_next >= hi_x;                                                                     \
+    }                                                                                            \
   } while (0)
 
-  // Scales and row flags were written with ordinary stores: make them visible
-  // before the first step (this also drains their global loads before the
-  // direct loads start counting).
-  __syncthreads();
-  MOE_DMA(0, 0);
-  MOE_DMA(1, (1 < nk ? 1 : nk - 1));
-  MOE_DMA(2, (2 < nk ? 2 : nk - 1));
-  wait_vm_lgkm0<2 * NLD>();
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  Frags f0, f1;
-  MOE_LOAD(f0, 0, 0);
-  int st = 0;  // stage holding step k (read into registers during step k-1)
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    MOE_STEP(f0, f1, kt);
-    MOE_STEP(f1, f0, kt + 1);
-  }
-  if (kt < nk) MOE_STEP(f0, f1, kt);
+  // prologue: the first three k-steps, fully landed
+#pragma unroll
+  for (int q = 0; q < kStages; ++q) MOE_ISSUE(q);
   wait_vm_lgkm0<0>();
-#undef MOE_DMA
+  __syncthreads();
+  Frags f0, f1;
+  MOE_LOAD(f0, 0);
+  int st = 0;  // stage holding the current step (its fragments are in registers)
+  for (;;) {
+    MOE_STEP(f0, f1);
+    if (done) break;
+    MOE_STEP(f1, f0);
+    if (done) break;
+  }
+  MOE_EPILOGUE();
+  wait_vm_lgkm0<0>();  // the trailing re-reads and the stores
+#undef MOE_DSET
+#undef MOE_ISSUE
+#undef MOE_CSET
 #undef MOE_ROWOFF
 #undef MOE_LOAD
 #undef MOE_MMA
+#undef MOE_EPILOGUE
 #undef MOE_STEP
-  __syncthreads();
-
-  // ---- epilogue: accumulators -> bf16 tile in LDS -> row-contiguous stores ----------
-  constexpr int CROW = BN * 2 + 16;
-  uint8_t* Cs = smem;
-#pragma unroll
-  for (int jn = 0; jn < TN; ++jn)
-#pragma unroll
-    for (int im = 0; im < TM; ++im) {
-      const int m_local = wm * WM + im * 16 + frag_row;
-      const int n_local = wn * WN + jn * 16 + frag_k * 4;
-      const f32x4_t v = acc[jn][im];
-      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-      *reinterpret_cast<u32x2_t*>(Cs + m_local * CROW + n_local * 2) = u32x2_t{lo, hi};
-    }
-  __syncthreads();
-  constexpr int CPR = BN / 8;  // 16-byte chunks per output row
-  uint16_t* Cg = p.C + row0 * p.N + static_cast<int64_t>(nt) * BN;
-  for (int idx = tid; idx < BM * CPR; idx += kThreads) {
-    const int rr = idx / CPR, cc = idx - rr * CPR;
-    if (s_rowok[rr])
-      *reinterpret_cast<u32x4_t*>(Cg + static_cast<int64_t>(rr) * p.N + cc * 8) =
-          *reinterpret_cast<const u32x4_t*>(Cs + rr * CROW + cc * 16);
-  }
-  __syncthreads();  // the C tile and the row flags are reused by the next tile
-  }  // tile loop
 #endif
 }
 
@@ -471,7 +613,18 @@ static int persistent_grid() {
 
 template <int BM, int BN, bool FP8, bool MASKED>
 int32_t launch_gemm(GemmArgs a, hipStream_t s) {
+  // The run table holds one XCD's share of the M-tiles and tile positions are
+  // 32-bit: bound the M-tiles of the order (compact: about a million rows).
+  const int64_t m_tiles = (a.M + BM - 1) / BM;
+  const int64_t order_m = (MASKED ? a.G : 1) * m_tiles;
+  if (order_m > 8 * (kRunMax - 2)) return MOE_EUNSUPPORTED;
+  a.n_tiles = a.N / BN;
+  a.m_tiles = static_cast<int>(m_tiles);
+  const int64_t tiles = order_m * a.n_tiles;
+  if (tiles == 0) return MOE_OK;
+  if (tiles >= (1ll << 31)) return MOE_EUNSUPPORTED;
   constexpr int lds = gemm_lds_bytes<BM, BN, FP8>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -480,11 +633,6 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
       return MOE_EDEVICE;
     attr_set = true;
   }
-  a.n_tiles = a.N / BN;
-  a.m_tiles = static_cast<int>((a.M + BM - 1) / BM);
-  const int64_t tiles = static_cast<int64_t>(MASKED ? a.G : 1) * a.m_tiles * a.n_tiles;
-  if (tiles == 0) return MOE_OK;
-  if (tiles >= (1ll << 40)) return MOE_EINVAL;
   const int grid = persistent_grid();
   if (grid == 0) return MOE_EDEVICE;
   kern<<<grid, kThreads, lds, s>>>(a);
@@ -502,7 +650,7 @@ static int32_t validate_gemm(int32_t dtype, const void* A, const uint8_t* A_scal
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
   if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
-  if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && K > kMaxFp8K) return MOE_EUNSUPPORTED;
+  if (K > (1 << 22)) return MOE_EUNSUPPORTED;  // per-lane 32-bit source offsets
   if (!A || !B || !C) return MOE_EINVAL;
   return MOE_OK;
 }

@@ -100,6 +100,9 @@ def test_validation_rejects_before_launch():
     assert lib.silu_and_mul(P, 15, 128, None, P, 8, 0, P, None, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 33, 256, P, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 2, 100, P, None) == L.MOE_EUNSUPPORTED
+    # the on-chip run table bounds the M-tiles of the tile order
+    assert lib.grouped_gemm_contig(0, P, None, P, None, P, P, 8177 * 128, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 0, 4096, 256, 256, 256, None) == L.MOE_EUNSUPPORTED
     # masked tile prefix is held on chip for at most 1024 groups
     assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 8, 64, 256, 256, 1025, None) == L.MOE_EUNSUPPORTED
 
