@@ -60,6 +60,7 @@ def _load():
         "orc_route_topk": (None, [P, i32, i32, i32, P, P]),
         "orc_quant_rows": (None, [P, i64, i32, i64, P, P]),
         "orc_quant_weight_blocks": (None, [P, i32, i32, i32, P, P]),
+        "orc_requant_weight_blocks": (None, [P, P, i32, i32, i32, P, P]),
         "orc_scatter_compact": (i32, [P, i32, i32, P, i32, i32, i32, i32, i64, i32,
                                       P, P, P, P, P, P]),
         "orc_scatter_masked": (i32, [P, i32, i32, P, i32, i32, i32, i32, i32,
@@ -148,6 +149,19 @@ def quant_weight_blocks(w: np.ndarray):
     s = np.empty((G, N // 128, K // 128), np.uint8)
     _load().orc_quant_weight_blocks(_p(w), G, N, K, _p(q), _p(s))
     return q, s
+
+
+def requant_weight_blocks(q: np.ndarray, s: np.ndarray):
+    """Block-FP8 weights (e4m3 [G,N,K], fp32 scales [G,N/128,K/128]) -> the
+    UE8M0 block format (e4m3 [G,N,K], UE8M0 [G,N/128,K/128]) via bf16."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    G, N, K = q.shape
+    assert N % 128 == 0 and K % 128 == 0 and s.shape == (G, N // 128, K // 128)
+    qo = np.empty((G, N, K), np.uint8)
+    so = np.empty((G, N // 128, K // 128), np.uint8)
+    _load().orc_requant_weight_blocks(_p(q), _p(s), G, N, K, _p(qo), _p(so))
+    return qo, so
 
 
 def scatter_compact(x, topk_ids, expert_start, num_local_experts, block_e,

@@ -220,6 +220,29 @@ void orc_quant_weight_blocks(const uint16_t* w, int32_t G, int32_t N, int32_t K,
       }
 }
 
+/* P1 implementation breakdown item 1 (the standard MoE layer requantises both
+ * expert weight sets, w13 and w2, to UE8M0 block scales, with a bf16 output
+ * dtype): each element of a block-FP8 checkpoint is dequantised as
+ * decode(q) * s in fp32 (one fp32 rounding, as a tensor multiply in that
+ * dtype does) and rounded to bf16; the bf16 weights then take the same direct
+ * UE8M0 128x128 block quantisation as orc_quant_weight_blocks. */
+void orc_requant_weight_blocks(const uint8_t* q_in, const float* s_in, int32_t G, int32_t N,
+                               int32_t K, uint8_t* q_out, uint8_t* s_out) {
+  int32_t nb = N / 128, kb = K / 128;
+  int64_t n_el = (int64_t)G * N * K;
+  uint16_t* w = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n_el > 0 ? n_el : 1));
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_el; ++i) {
+    int64_t g = i / ((int64_t)N * K);
+    int64_t n = (i / K) % N, k = i % K;
+    float s = s_in[(g * nb + n / 128) * kb + k / 128];
+    float v = (float)orc_e4m3_to_f64(q_in[i]) * s;  /* fp32 product */
+    w[i] = orc_f64_to_bf16((double)v);
+  }
+  orc_quant_weight_blocks(w, G, N, K, q_out, s_out);
+  free(w);
+}
+
 /* ------------------------------------------------------------------------ */
 /* scatter                                                                   */
 /* ------------------------------------------------------------------------ */

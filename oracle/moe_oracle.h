@@ -52,6 +52,10 @@ void orc_quant_rows(const uint16_t* x, int64_t M, int32_t K, int64_t ld_x,
 /* Same rule over 128x128 blocks of w[G][N][K]. */
 void orc_quant_weight_blocks(const uint16_t* w, int32_t G, int32_t N, int32_t K,
                              uint8_t* q, uint8_t* scale);
+/* Requantise block-FP8 weights (e4m3 codes, fp32 scale per 128x128 block) to
+ * UE8M0 block scales through a bf16 intermediate. */
+void orc_requant_weight_blocks(const uint8_t* q_in, const float* s_in, int32_t G, int32_t N,
+                               int32_t K, uint8_t* q_out, uint8_t* s_out);
 
 /* Compact layout (P1 implementation breakdown items 2-4). Returns 0, or 3 when
  * rows_capacity is below the rows the routing needs.  fp8 != 0 quantises each
