@@ -37,17 +37,19 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the timed oracle run on the host")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run w13 and SiLU-and-mul as two kernels")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
-def build_layer(wl, torch):
+def build_layer(wl, torch, fuse_silu=True):
     from scatter_grouped_gemm_amd import MoELayer, inputs
     layer = MoELayer(hidden=wl.H, intermediate=wl.I, num_experts=wl.E, top_k=wl.k, max_tokens=wl.T,
                      num_local_experts=wl.El, expert_start=wl.expert_start, fp8=wl.fp8,
                      layout=wl.layout, block_e=wl.block_e, max_m=wl.max_m or None,
-                     expected_m=wl.expected_m, device="cuda")
+                     expected_m=wl.expected_m, fuse_silu=fuse_silu, device="cuda")
     t0 = time.time()
     for e in range(wl.El):
         w13, w2 = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
@@ -62,7 +64,9 @@ def build_layer(wl, torch):
 
 def gemm_work(wl, layer, torch):
     """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs for the valid
-    rows of this batch (padding rows excluded)."""
+    rows of this batch (padding rows excluded).  With SiLU-and-mul fused into
+    w13 its output is the activation (I channels, e4m3 + scales or bf16)
+    instead of the bf16 gate/up pair."""
     if layer.layout == "compact":
         counts = layer.num_valid.cpu().to(torch.int64)
     else:
@@ -75,7 +79,8 @@ def gemm_work(wl, layer, torch):
     w2_flops = 2.0 * A * H * I
     sc = (1.0 / (128 * 128)) if wl.fp8 else 0.0          # weight block scales
     asc = (1.0 / 128) if wl.fp8 else 0.0                 # activation scales
-    w13_bytes = active * 2 * I * H * (ab + sc) + A * H * (ab + asc) + A * 2 * I * 2
+    w13_out = (I * (ab + asc)) if layer.fuse_silu else (2 * I * 2)
+    w13_bytes = active * 2 * I * H * (ab + sc) + A * H * (ab + asc) + A * w13_out
     w2_bytes = active * H * I * (ab + sc) + A * I * (ab + asc) + A * H * 2
     return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
                 w13_bytes=w13_bytes, w2_bytes=w2_bytes)
@@ -203,7 +208,7 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del a, b
-    layer, x, logits = build_layer(wl, torch)
+    layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused)
     for _ in range(args.warmup):
         layer(x, logits)
     torch.cuda.synchronize()
@@ -221,12 +226,14 @@ def main():
     log(f"{ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
     work = gemm_work(wl, layer, torch)
     dtype = "fp8_e4m3" if wl.fp8 else "bf16"
-    roof = roofline(work["w13_flops"], work["w13_bytes"], kern["gemm_w13"], dtype)
-    roof["kernel"] = "grouped_gemm w13 (gate/up)"
+    w13_key = "gemm_w13_silu" if layer.fuse_silu else "gemm_w13"
+    roof = roofline(work["w13_flops"], work["w13_bytes"], kern[w13_key], dtype)
+    roof["kernel"] = ("grouped_gemm w13 (gate/up) with SiLU-and-mul" if layer.fuse_silu
+                      else "grouped_gemm w13 (gate/up)")
     roof["traffic"] = measured_traffic(wl.name, "w13")
     w2_roof = roofline(work["w2_flops"], work["w2_bytes"], kern["gemm_w2"], dtype)
     w2_roof["traffic"] = measured_traffic(wl.name, "w2")
-    gemm_ms = kern["gemm_w13"] + kern["gemm_w2"]
+    gemm_ms = kern[w13_key] + kern["gemm_w2"]
     gemm_tflops = (work["w13_flops"] + work["w2_flops"]) / (gemm_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -243,7 +250,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) expert weights)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
                    "E_local": wl.El, "top_k": wl.k, "layout": layer.layout, "block_e": wl.block_e,
-                   "rows": layer.rows, "assignments": work["assignments"]},
+                   "rows": layer.rows, "assignments": work["assignments"],
+                   "silu_fused_into_w13": layer.fuse_silu},
         "roofline": roof,
         "gemm": {"tflops_both": round(gemm_tflops, 1),
                  "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),

@@ -178,6 +178,19 @@ int32_t moe_quant_fp8_ue8m0(const void* x, int64_t M, int32_t K, int64_t ld_x,
 int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t N, int32_t K,
                                    uint8_t* q, uint8_t* scale, void* stream);
 
+/* Requantise block-FP8 expert weights (a checkpoint's e4m3 codes with one
+ * fp32 scale per 128x128 block) to the UE8M0 block format, through a bf16
+ * intermediate ("Support DeepGEMM for standard MoE dispatch", implementation
+ * breakdown item 1: both w13 and w2 of the standard layer are requantised with
+ * bf16 as the output dtype): w = bf16(decode(q) * s) in fp32, then exactly
+ * moe_quant_weight_fp8_ue8m0 of w.
+ *   q_in   device e4m3 [G][N][K];  s_in  device fp32 [G][N/128][K/128]
+ *   q_out  device e4m3 [G][N][K] (may be q_in);  s_out  device u8 [G][N/128][K/128]
+ *   Non-finite codes or products give unspecified results.
+ * Limits: N % 128 == 0, K % 128 == 0. */
+int32_t moe_requant_weight_fp8_ue8m0(const uint8_t* q_in, const float* s_in, int32_t G, int32_t N,
+                                     int32_t K, uint8_t* q_out, uint8_t* s_out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped GEMMs ("NT": C = A . B[g]^T), fp32 accumulation, bf16 output
  * ------------------------------------------------------------------------- */
@@ -210,12 +223,36 @@ int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale
  *               0 = no hint.
  *   Rows at or past masked_m[g] receive unspecified values, except that rows
  *   at or past masked_m[g] rounded up to 128 are never written.
- * Limits: N, K as grouped_gemm_contig; G <= 1024; G * ceil(max_m / tile
- * height) <= 8176 -> else MOE_EUNSUPPORTED. */
+ * Limits: N, K as grouped_gemm_contig; G <= 1024; the tile count, at most
+ * G * ceil(max_m / 64) * N / 128, below 2^31 -> else MOE_EUNSUPPORTED. */
 int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
                             const void* B, const uint8_t* B_scale, void* C,
                             const int32_t* masked_m, int32_t expected_m, int32_t max_m,
                             int32_t N, int32_t K, int32_t G, void* stream);
+
+/* The w13 GEMM with SiLU-and-mul in its epilogue (the two steps of P2 key
+ * source excerpt _run_bf16_contiguous_gemm, w13 then silu_and_mul, in one
+ * pass): B is w13 [G][2I][K] (gate rows [0, I), up rows [I, 2I)) and the
+ * result is the activation act[r][i] = silu(C[r][i]) * C[r][I + i] with
+ * C = A . B[g]^T rounded to bf16 first, exactly as grouped_gemm_* followed by
+ * silu_and_mul computes it (bit for bit).
+ *   out_dtype  MOE_DTYPE_BF16: out bf16 [rows][I];
+ *              MOE_DTYPE_FP8_E4M3_UE8M0: out e4m3 [rows][I] with out_scale
+ *              laid out as silu_and_mul's (compact [I/128][M], masked
+ *              [G][I/128][max_m]).
+ *   Rows follow the underlying GEMM: rows of blocks whose first row is -1
+ *   (compact) or at or past masked_m rounded up to 128 (masked) are not
+ *   written; other rows past an expert's valid rows receive unspecified values.
+ * Limits: I % 128 == 0, I <= 2^29; the rest as the underlying GEMM. */
+int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                 const void* B, const uint8_t* B_scale, int32_t out_dtype,
+                                 void* out, uint8_t* out_scale, const int32_t* m_indices,
+                                 int64_t M, int32_t I, int32_t K, int32_t G, void* stream);
+int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                 const void* B, const uint8_t* B_scale, int32_t out_dtype,
+                                 void* out, uint8_t* out_scale, const int32_t* masked_m,
+                                 int32_t expected_m, int32_t max_m, int32_t I, int32_t K,
+                                 int32_t G, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Activation and combine
@@ -223,8 +260,9 @@ int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale
 
 /* SiLU-and-mul, P2 key source excerpt of _run_bf16_contiguous_gemm (the w13
  * output [M][2I] is halved): out[r][i] = silu(gateup[r][i]) * gateup[r][I+i],
- * computed in fp32 and rounded to bf16; for FP8 output that bf16 row is then
- * quantised as moe_quant_fp8_ue8m0 does.
+ * computed in fp32 (silu(g) = g * 1/(1 + 2^(-g log2 e)) with the hardware
+ * exp2 and reciprocal, each within about one fp32 ulp) and rounded to bf16;
+ * for FP8 output that bf16 row is then quantised as moe_quant_fp8_ue8m0 does.
  *   Row selection: m_indices (compact; rows with -1 skipped) or masked_m with
  *   max_m (masked; M = G*max_m, rows r % max_m >= masked_m[r / max_m] skipped);
  *   both NULL = every row.

@@ -35,8 +35,13 @@ SIGNATURES = {
                                   _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_quant_fp8_ue8m0": (_I32, [_P, _I64, _I32, _I64, _P, _P, _P, _P]),
     "moe_quant_weight_fp8_ue8m0": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_requant_weight_fp8_ue8m0": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "grouped_gemm_contig": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "grouped_gemm_masked": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "grouped_gemm_contig_silu": (_I32, [_I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32,
+                                        _I32, _P]),
+    "grouped_gemm_masked_silu": (_I32, [_I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
+                                        _I32, _I32, _P]),
     "silu_and_mul": (_I32, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _P, _P, _I32, _I32, _I32, _P, _P]),
 }
@@ -158,6 +163,15 @@ def moe_quant_weight_fp8_ue8m0(w, q, scale):
         _ptr(w), G, N, K, _ptr(q), _ptr(scale), _stream()))
 
 
+def moe_requant_weight_fp8_ue8m0(q_in, s_in, q_out, s_out):
+    """Block-FP8 weights (e4m3 [G,N,K] + fp32 [G,N/128,K/128]) -> e4m3 + UE8M0."""
+    G, N, K = q_in.shape
+    assert q_in.dtype == torch.uint8 and s_in.dtype == torch.float32 and q_out.shape == (G, N, K)
+    assert s_in.shape == (G, N // 128, K // 128) and s_out.shape == s_in.shape and s_out.dtype == torch.uint8
+    _check("moe_requant_weight_fp8_ue8m0", lib().moe_requant_weight_fp8_ue8m0(
+        _ptr(q_in), _ptr(s_in), G, N, K, _ptr(q_out), _ptr(s_out), _stream()))
+
+
 def grouped_gemm_contig(fp8, A, A_scale, B, B_scale, C, m_indices):
     M, K = A.shape
     G, N, K2 = B.shape
@@ -174,6 +188,33 @@ def grouped_gemm_masked(fp8, A, A_scale, B, B_scale, C, masked_m, expected_m):
     _check("grouped_gemm_masked", lib().grouped_gemm_masked(
         _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(masked_m),
         expected_m, max_m, N, K, G, _stream()))
+
+
+def grouped_gemm_contig_silu(fp8, A, A_scale, B, B_scale, out, m_indices, out_scale=None):
+    """w13 GEMM with SiLU-and-mul fused: out [M][I] is bf16, or e4m3 (uint8)
+    with out_scale [I/128][M]."""
+    M, K = A.shape
+    G, N, K2 = B.shape
+    I = N // 2
+    q8 = out.dtype == torch.uint8
+    assert K == K2 and out.shape == (M, I) and (q8 or out.dtype == torch.bfloat16)
+    _check("grouped_gemm_contig_silu", lib().grouped_gemm_contig_silu(
+        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
+        _ptr(out), _ptr(out_scale), _ptr(m_indices), M, I, K, G, _stream()))
+
+
+def grouped_gemm_masked_silu(fp8, A, A_scale, B, B_scale, out, masked_m, expected_m,
+                             out_scale=None):
+    """Masked-layout w13 GEMM with SiLU-and-mul fused: out [G][max_m][I];
+    FP8 out_scale [G][I/128][max_m]."""
+    G, max_m, K = A.shape
+    G2, N, K2 = B.shape
+    I = N // 2
+    q8 = out.dtype == torch.uint8
+    assert G == G2 and K == K2 and out.shape == (G, max_m, I) and (q8 or out.dtype == torch.bfloat16)
+    _check("grouped_gemm_masked_silu", lib().grouped_gemm_masked_silu(
+        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
+        _ptr(out), _ptr(out_scale), _ptr(masked_m), expected_m, max_m, I, K, G, _stream()))
 
 
 def silu_and_mul(gateup, out, fp8=False, out_scale=None, m_indices=None, masked_m=None, max_m=0):

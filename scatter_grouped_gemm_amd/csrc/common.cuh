@@ -33,25 +33,19 @@ __device__ __forceinline__ int ue8m0_exponent(float amax) {
   return e < -126 ? -126 : (e > 127 ? 127 : e);
 }
 
-// e4m3fn (OCP, bias 7) of an fp32 value, round to nearest even, saturating to
-// +-448, sign of zero kept.  Integer arithmetic on the fp32 encoding, so the
-// result does not depend on conversion-instruction modes.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;                       // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;               // >= 448 (incl. inf)
-  if (a < 0x3c800000u) {                                   // < 2^-6: subnormal grid 2^-9
-    float q = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
-    return sign | static_cast<uint32_t>(q);                // 8 -> 0x08 = 2^-6
-  }
-  uint32_t exp = (a >> 23) - 127u + 7u;                    // 1..15
-  uint32_t m = (a >> 20) & 7u;
-  uint32_t rem = a & 0xfffffu;
-  m += (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ? 1u : 0u;
-  uint32_t code = (exp << 3) + m;                          // carry m==8 into exponent
-  return sign | (code > 0x7eu ? 0x7eu : code);
+// Four fp32 values times 2^-e as e4m3fn (OCP, bias 7) codes packed
+// little-endian, rounded to nearest even with the sign of zero kept, by the
+// hardware conversion (two values per instruction).  For |v * 2^-e| <= 448,
+// which a UE8M0 exponent from ue8m0_exponent of the group maximum guarantees
+// for finite groups, this is the exact RNE encoding (the conversion matches an
+// integer implementation of it on every fp32 bit pattern in that range);
+// larger magnitudes and NaN give the NaN code 0x7f.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, int e) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(a, -e),
+                                          __builtin_amdgcn_ldexpf(b, -e), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(c, -e),
+                                      __builtin_amdgcn_ldexpf(d, -e), w, true);
+  return static_cast<uint32_t>(w);
 }
 
 template <typename T>
@@ -70,6 +64,27 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 __device__ __forceinline__ unsigned long long ballot(bool p) { return __ballot(p); }
+
+// e4m3fn (OCP, bias 7) code -> fp32, exact: exponent field 0 holds the
+// subnormals m * 2^-9, 0x7f / 0xff are NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t em = c & 0x7fu;
+  if (em == 0x7fu) return __uint_as_float(sign | 0x7fc00000u);
+  const uint32_t e = em >> 3, m = em & 7u;
+  const float v = e == 0 ? static_cast<float>(m) * (1.0f / 512.0f)
+                         : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(v) | sign);
+}
+
+// SiLU in fp32: g * 1 / (1 + e^-g), with e^-g as 2^(-g log2 e) and the
+// reciprocal from the hardware approximations (each within about one fp32 ulp),
+// so that it stays a handful of instructions.  Every kernel that computes the
+// activation uses this one definition, which keeps them bit-identical.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 }  // namespace moe
 

@@ -39,9 +39,10 @@
 //     each with its own L2).  Compact layout: a run is a maximal range of
 //     M-tiles whose first rows carry one id (BM divides the 128-row alignment,
 //     so a tile never straddles experts); masked layout: group g has
-//     ceil(masked_m[g] / BM) tiles.  Every workgroup first writes a table of
-//     the runs covering its XCD's share into LDS, so finding a tile's expert
-//     and offsets costs a few LDS reads, never a global load inside the loop.
+//     ceil(masked_m[g] / BM) tiles.  Every workgroup first writes into LDS a
+//     table of the runs covering its XCD's share (compact) or the prefix sums
+//     of the group tile counts (masked), so finding a tile's expert and
+//     offsets costs a few LDS reads, never a global load inside the loop.
 //   - Batch invariance: the instruction shape and the k order are the same for
 //     every tile size and layout; a row's result depends only on its own A row
 //     and its expert's weights.
@@ -63,7 +64,8 @@ struct GemmArgs {
   const uint8_t* A_scale;
   const uint8_t* B;
   const uint8_t* B_scale;
-  uint16_t* C;
+  void* C;                 // bf16 [rows][N]; fused SiLU-and-mul: the activation [rows][N/2]
+  uint8_t* C_scale;        // fused SiLU-and-mul with FP8 output: its UE8M0 scales
   const int32_t* rowinfo;  // m_indices (contiguous) or masked_m (masked)
   int64_t M;               // contiguous: rows of A/C; masked: max_m
   int N, K, G;
@@ -71,20 +73,33 @@ struct GemmArgs {
   int n_tiles;
 };
 
+// Epilogues: the bf16 product, or SiLU-and-mul of its two halves (gate =
+// columns [0, N/2), up = [N/2, N)) written as bf16 or as e4m3 + UE8M0.
+constexpr int kEpiPlain = 0, kEpiSiluBf16 = 1, kEpiSiluFp8 = 2;
+
 constexpr int kWaves = 8;             // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 3;
-constexpr int kScaleArea = kWaves * 256;  // FP8: one 64-dword slot per wavefront per stage
+constexpr int kScaleSlot = 256;      // FP8: 64 dwords, one 1-byte load per lane
 constexpr int kRunMax = 1024;         // run-table entries: M-tiles of one XCD's share
 constexpr int kMaxMaskedGroups = 1024;
+// masked layout: prefix sums of the group tile counts, padded so that the
+// two-level search below reads in bounds
+constexpr int kPrefixLen = kMaxMaskedGroups + 17;
+static_assert(kPrefixLen * 4 <= kRunMax * 8, "the prefix array lives in the run-table space");
 
+// Stage: the data rows, then for FP8 the scale slots of the BM/64 wavefronts
+// fetching activation scales and one shared by the rest (weight scales).
 template <int BM, int BN, bool FP8>
 constexpr int gemm_stage_bytes() {
-  return (BM + BN) * 128 + (FP8 ? kScaleArea : 0);
+  return (BM + BN) * 128 + (FP8 ? (BM / 64 + 1) * kScaleSlot : 0);
 }
-template <int BM, int BN, bool FP8>
+// LDS: stages, the run table and, for the FP8 SiLU epilogue, the per-row
+// maxima of the column wavefronts.
+template <int BM, int BN, bool FP8, int EPI>
 constexpr int gemm_lds_bytes() {
-  return kStages * gemm_stage_bytes<BM, BN, FP8>() + kRunMax * 8;
+  return kStages * gemm_stage_bytes<BM, BN, FP8>() + kRunMax * 8 +
+         (EPI == kEpiSiluFp8 ? BM * (kWaves / (BM >= 128 ? 2 : 1)) * 4 : 0);
 }
 
 // chunk permutation of LDS stage row r (see the kernel's staging comment)
@@ -124,15 +139,58 @@ __device__ __forceinline__ int2 read_table(const int2* table, int j) {
   asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ void lds_write_b64(const void* p, u32x2_t v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_b32(const void* p, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x4_t lds_read_b128(const void* p) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ int lds_read_b32(const void* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+// Masked layout: pre[g] = M-tiles of the groups before g (pre[G] = used, then
+// INT_MAX up to kPrefixLen).  The group of M-tile i is the last g with
+// pre[g] <= i (empty groups repeat a value and are passed over): lane j first
+// tests pre[16 j], then pre[16 c + j] inside the 16-group window c found.
+template <bool MASKED>
 __device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_tiles, int used,
                                            int pos) {
   TilePos t;
   const int i0 = pos / n_tiles;
-  const int2 e = read_table(table, i0 - i_lo);
-  const int x = __builtin_amdgcn_readfirstlane(e.x);
-  t.g = __builtin_amdgcn_readfirstlane(e.y);
-  t.first = i_lo + static_cast<int>(static_cast<int16_t>(x & 0xffff));
-  const int run = i_lo + (x >> 16) - t.first;
+  int run;
+  if constexpr (MASKED) {
+    const int* const pre = reinterpret_cast<const int*>(table);
+    const int lane = __lane_id();
+    const int c = __builtin_popcountll(ballot(lds_read_b32(pre + 16 * lane) <= i0)) - 1;
+    const int v = lds_read_b32(pre + 16 * c + (lane <= 16 ? lane : 16));
+    const int c2 = __builtin_popcountll(ballot(lane <= 16 && v <= i0)) - 1;
+    if (c < 0 || c2 < 0 || c2 > 15) {
+      t.g = -1;  // cannot happen: pre[0] = 0 <= i0 < pre[16 c + 16]
+      t.nt = 0;
+      t.mt = 0;
+      t.first = 0;
+      return t;
+    }
+    t.g = 16 * c + c2;
+    t.first = __builtin_amdgcn_readlane(v, c2);
+    run = __builtin_amdgcn_readlane(v, c2 + 1) - t.first;
+  } else {
+    const int2 e = read_table(table, i0 - i_lo);
+    const int x = __builtin_amdgcn_readfirstlane(e.x);
+    t.g = __builtin_amdgcn_readfirstlane(e.y);
+    t.first = i_lo + static_cast<int>(static_cast<int16_t>(x & 0xffff));
+    run = i_lo + (x >> 16) - t.first;
+  }
   const int local = pos - t.first * n_tiles;
   if (run <= 0 || t.first < 0 || t.first + run > used || local < 0 || local >= run * n_tiles) {
     t.g = -1;  // an inconsistent entry is never used (cannot happen for a well-built table)
@@ -147,10 +205,11 @@ __device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_ti
 
 // First position at or after pos (stepping by `stride`) whose run is a valid
 // expert, or a position >= end.
+template <bool MASKED>
 __device__ __forceinline__ int next_tile(const int2* table, int i_lo, int n_tiles, int used, int G,
                                          int pos, int end, int stride) {
   for (; pos < end; pos += stride) {
-    const TilePos t = map_pos(table, i_lo, n_tiles, used, pos);
+    const TilePos t = map_pos<MASKED>(table, i_lo, n_tiles, used, pos);
     if (t.g >= 0 && t.g < G) break;
   }
   return pos;
@@ -176,7 +235,7 @@ __device__ __forceinline__ void tile_rows(const GemmArgs& p, const TilePos& t, i
   }
 }
 
-template <int BM, int BN, bool FP8, bool MASKED>
+template <int BM, int BN, bool FP8, bool MASKED, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
@@ -194,6 +253,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
                 "tile shape");
   static_assert(ROWS % (8 * kWaves) == 0, "stage rows split evenly over the wavefronts");
   static_assert(ASW < kWaves, "a wavefront is left for the weight scales");
+  // The SiLU epilogue takes gate block nt and up block nt into one tile, laid
+  // out in the stage as chunks of CH = WN/2 rows gate, up, gate, up, ... so
+  // that every wavefront holds CH gate columns and the matching CH up columns
+  // (sub-tiles jn < TN/2: gate, jn + TN/2: the same channels of up).
+  constexpr int CH = WN / 2;
+  static_assert(EPI == kEpiPlain || (BN == 256 && (WN == 64 || WN == 32)), "SiLU tile shape");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int2* const table = reinterpret_cast<int2*>(smem + kStages * STAGE);
   int* const scratch = reinterpret_cast<int*>(smem);  // set-up only (stage memory)
@@ -219,7 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     used = __builtin_amdgcn_readfirstlane(last + 1);
     __syncthreads();  // scratch is rewritten below
   } else {
-    // scratch[g] = M-tiles of the groups before g, scratch[G] = total
+    // pre[g] = M-tiles of the groups before g, pre[G] = total, then INT_MAX
+    int* const pre = reinterpret_cast<int*>(table);
     constexpr int PER = (kMaxMaskedGroups + kThreads - 1) / kThreads;
     int* const wsum = scratch + kMaxMaskedGroups + 8;
     int cnt[PER];
@@ -249,12 +315,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int g = tid * PER + i;
-      if (g < p.G) scratch[g] = base;
+      if (g < p.G) pre[g] = base;
       base += cnt[i];
     }
-    if (tid == kThreads - 1) scratch[p.G] = base;  // groups >= G count 0
+    if (tid == kThreads - 1) pre[p.G] = base;  // groups >= G count 0
+    for (int g = p.G + 1 + tid; g < kPrefixLen; g += kThreads) pre[g] = INT_MAX;
     __syncthreads();
-    used = __builtin_amdgcn_readfirstlane(scratch[p.G]);
+    used = __builtin_amdgcn_readfirstlane(pre[p.G]);
   }
   // XCD x (= blockIdx % 8) takes the x-th eighth [lo_x, hi_x) of the order;
   // its workgroups step through it side by side.
@@ -265,9 +332,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int hi_x = static_cast<int>((static_cast<int64_t>(U) * (xcd + 1)) >> 3);
   if (lo_x + static_cast<int>(blockIdx.x >> 3) >= hi_x) return;
   const int i_lo = lo_x / n_tiles;
-  const int R = (hi_x - 1) / n_tiles - i_lo + 1;  // <= kRunMax (host bound)
+  const int R = (hi_x - 1) / n_tiles - i_lo + 1;  // compact: <= kRunMax (host bound)
 
-  // ---- run table for M-tiles [i_lo, i_lo + R) ----
+  // ---- compact: run table for M-tiles [i_lo, i_lo + R) ----
   if (!MASKED) {
     int* const ids = scratch + 8;                  // [R]
     int* const wred = scratch + 8 + kRunMax;       // [2 * kWaves]
@@ -337,18 +404,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       table[2 * tid] = make_int2(((f0 - i_lo) & 0xffff) | ((e0 - i_lo) << 16), id[0]);
     if (2 * tid + 1 < R)
       table[2 * tid + 1] = make_int2(((f1 - i_lo) & 0xffff) | ((e1 - i_lo) << 16), id[1]);
-  } else {
-    const int* const pre = scratch;
-    for (int j = tid; j < R; j += kThreads) {
-      const int i = i_lo + j;
-      int lo = 0, hi = p.G;  // last group whose prefix is <= i
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= i) lo = mid;
-        else hi = mid;
-      }
-      table[j] = make_int2(((pre[lo] - i_lo) & 0xffff) | ((pre[lo + 1] - i_lo) << 16), lo);
-    }
   }
   __syncthreads();  // table complete; stage memory is free
 
@@ -360,11 +415,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int G = p.G;
 
   // -- load side: the tile and k-step whose stage is filled next --
-  int d_pos = next_tile(table, i_lo, n_tiles, used, G, lo_x + static_cast<int>(blockIdx.x >> 3),
+  int d_pos = next_tile<MASKED>(table, i_lo, n_tiles, used, G, lo_x + static_cast<int>(blockIdx.x >> 3),
                                 hi_x, per_xcd);
   if (d_pos >= hi_x) return;
   int d_k = 0;
   int64_t d_aoff, d_boff, d_as0, d_bs0;  // byte offsets of the tile in A and B; scale indices
+  // B columns (weight rows) a tile advances by per N-tile, and the distance in
+  // the weight-scale array between the tile's two 128-column blocks
+  constexpr int NBW = EPI == kEpiPlain ? BN : 128;
+  const int64_t bs_stride = EPI == kEpiPlain ? KB : static_cast<int64_t>(p.N / 256) * KB;
   int d_rows;
   uint32_t soff[NLD];  // per-lane source offsets from the tile's A / B rows
   // A direct load moves 8 rows (64 lanes x 16 bytes) into LDS; lane i carries
@@ -372,17 +431,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // chunk (i & 7) ^ swz(row).  Stage rows [0, BM) are A rows, [BM, ROWS) B rows.
 #define MOE_DSET(pos_)                                                                        \
   do {                                                                                        \
-    const TilePos t_ = map_pos(table, i_lo, n_tiles, used, (pos_));                                 \
+    const TilePos t_ = map_pos<MASKED>(table, i_lo, n_tiles, used, (pos_));                         \
     int64_t r0_;                                                                              \
     tile_rows<BM, MASKED>(p, t_, r0_, d_rows, d_as0);                                         \
     d_pos = (pos_);                                                                           \
     d_aoff = r0_ * rowbytes;                                                                  \
-    d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * BN) * rowbytes; \
-    d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * NB) * KB;                     \
+    d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * NBW) * rowbytes; \
+    d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * (NBW / 128)) * KB;            \
     _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                         \
       const int R_ = (wave * NLD + j) * 8 + (lane >> 3);                                      \
       const int c_ = (lane & 7) ^ lds_swz(R_);                                                \
-      const int r_ = R_ < BM ? (R_ < d_rows ? R_ : d_rows - 1) : R_ - BM;                     \
+      int r_ = R_ < BM ? (R_ < d_rows ? R_ : d_rows - 1) : R_ - BM;                           \
+      if (EPI != kEpiPlain && R_ >= BM)                                                       \
+        r_ = ((r_ / CH) & 1) * (p.N / 2) + (r_ / (2 * CH)) * CH + (r_ % CH);                  \
       soff[j] = static_cast<uint32_t>(r_ * rowbytes + c_ * 16);                               \
     }                                                                                         \
   } while (0)
@@ -390,7 +451,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 
   // One k-step of loads into stage st_: for FP8 first the scale bytes (wave w
   // < ASW: activation scales of tile rows 64w..64w+63; wave ASW: the NB
-  // weight-block scales; the rest repeat those), then the data rows.
+  // weight-block scales; the rest repeat those into the same slot), then the
+  // data rows.
 #define MOE_ISSUE(st_)                                                                          \
   do {                                                                                          \
     uint8_t* const stg_ = smem + (st_) * STAGE;                                                 \
@@ -402,10 +464,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
         src_ = p.A_scale + d_as0 + static_cast<int64_t>(d_k) * p.M + r_;                       \
       } else {                                                                                  \
         const int nb_ = lane < NB ? lane : NB - 1;                                              \
-        src_ = p.B_scale + d_bs0 + static_cast<int64_t>(nb_) * KB + d_k;                        \
+        src_ = p.B_scale + d_bs0 + nb_ * bs_stride + d_k;                                       \
       }                                                                                         \
+      /* wavefronts past ASW all write the same bytes into one slot */                          \
       __builtin_amdgcn_global_load_lds(src_,                                                    \
-          (__attribute__((address_space(3))) void*)(stg_ + SDATA + wave * 256), 1, 0, 0);       \
+          (__attribute__((address_space(3))) void*)(stg_ + SDATA + (wave < ASW ? wave : ASW) * kScaleSlot), \
+          1, 0, 0);                                                                             \
     }                                                                                           \
     const uint8_t* ab_ = p.A + d_aoff + static_cast<int64_t>(d_k) * 128;                        \
     const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * 128;                        \
@@ -418,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     /* advance; past the last tile keep re-reading its last k-step (never used) */             \
     if (++d_k == nk) {                                                                          \
       d_k = 0;                                                                                  \
-      const int np_ = next_tile(table, i_lo, n_tiles, used, G, d_pos + per_xcd, hi_x, per_xcd); \
+      const int np_ = next_tile<MASKED>(table, i_lo, n_tiles, used, G, d_pos + per_xcd, hi_x, per_xcd); \
       if (np_ < hi_x) MOE_DSET(np_);                                                            \
       else d_k = nk - 1;                                                                        \
     }                                                                                           \
@@ -427,15 +491,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // -- compute side: the tile being accumulated --
   int c_k = 0;
   int c_pos = d_pos;
-  int c_next = next_tile(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);
+  int c_next = next_tile<MASKED>(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);
   int64_t c_row0;
-  int c_rows, c_nt;
+  int c_rows, c_nt, c_g;
 #define MOE_CSET(pos_)                                                                        \
   do {                                                                                        \
-    const TilePos t_ = map_pos(table, i_lo, n_tiles, used, (pos_));                                 \
+    const TilePos t_ = map_pos<MASKED>(table, i_lo, n_tiles, used, (pos_));                         \
     int64_t as0_;                                                                             \
     tile_rows<BM, MASKED>(p, t_, c_row0, c_rows, as0_);                                       \
     c_nt = t_.nt;                                                                             \
+    c_g = t_.g;                                                                               \
     c_pos = (pos_);                                                                           \
   } while (0)
   MOE_CSET(c_pos);
@@ -462,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     frag_t a[KS][TM];
     frag_t b[KS][TN];
     int sa[TM];
-    int sw;
+    int sw, sw2;  // weight scales of the wavefront's columns (SiLU: gate, up)
   };
 #define MOE_LOAD(F_, st_)                                                                        \
   do {                                                                                           \
@@ -495,7 +560,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       const uint8_t* X_ = S_ + SDATA;                                                            \
       _Pragma("unroll") for (int im = 0; im < TM; ++im)                                          \
         F_.sa[im] = X_[(wm * WM + im * 16 + frag_row) * 4];                                      \
-      F_.sw = X_[ASW * 256 + wblk * 4];                                                          \
+      F_.sw = X_[ASW * kScaleSlot + (EPI == kEpiPlain ? wblk : 0) * 4];                          \
+      F_.sw2 = X_[ASW * kScaleSlot + 4];                                                         \
     }                                                                                            \
   } while (0)
 #define MOE_MMA(F_)                                                                              \
@@ -505,7 +571,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
         _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
           if constexpr (FP8)                                                                     \
             acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                      \
-                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], 0, 0, 0, F_.sw, 0, F_.sa[im]);          \
+                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], 0, 0, 0,                                \
+                (EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw, 0, F_.sa[im]);              \
           else                                                                                   \
             acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F_.b[ks][jn], F_.a[ks][im],    \
                                                                   acc[jn][im], 0, 0, 0);         \
@@ -513,21 +580,116 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   } while (0)
   // Stores of the finished compute tile (lane: 4 consecutive columns of a row
   // per 16x16 block), then a fresh accumulator.
+  //   Plain: the bf16 product.
+  //   SiLU: per row and channel c of the tile's 128-channel block nt, gate and
+  //   up (sub-tiles jn and jn + TN/2 of the lane) are rounded to bf16 as the
+  //   plain product would be stored, act = bf16(silu(gate) * up) in fp32 (the
+  //   same silu_f32 as the stand-alone SiLU-and-mul); FP8 output
+  //   then takes the row's maximum over the 128 channels (the four column
+  //   wavefronts of the row meet in LDS) and quantises as moe_quant_fp8_ue8m0.
+  float* const rowmax = reinterpret_cast<float*>(smem + kStages * STAGE + kRunMax * 8);
 #define MOE_EPILOGUE()                                                                           \
   do {                                                                                           \
-    uint16_t* const cg_ = p.C + c_row0 * p.N + static_cast<int64_t>(c_nt) * BN + wn * WN + frag_k * 4; \
-    _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                          \
-      const int r_ = wm * WM + im * 16 + frag_row;                                               \
-      if (r_ < c_rows) {                                                                         \
-        uint16_t* const crow_ = cg_ + static_cast<int64_t>(r_) * p.N;                            \
-        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                      \
-          const f32x4_t v_ = acc[jn][im];                                                        \
-          const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                       \
-                               (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);                \
-          const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                       \
-                               (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);                \
-          *reinterpret_cast<u32x2_t*>(crow_ + jn * 16) = u32x2_t{lo_, hi_};                      \
+    /* lane indices from an opaque copy: rebuilt here rather than held in */                     \
+    /* registers across the main loop                                    */                     \
+    int te_ = threadIdx.x;                                                                       \
+    asm volatile("" : "+v"(te_));                                                                \
+    const int frag_row = te_ & 15;                                                               \
+    const int frag_k = (te_ >> 4) & 3;                                                           \
+    if constexpr (EPI == kEpiPlain) {                                                            \
+      uint16_t* const cg_ = static_cast<uint16_t*>(p.C) + c_row0 * p.N +                         \
+                            static_cast<int64_t>(c_nt) * BN + wn * WN + frag_k * 4;              \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                        \
+        const int r_ = wm * WM + im * 16 + frag_row;                                             \
+        if (r_ < c_rows) {                                                                       \
+          uint16_t* const crow_ = cg_ + static_cast<int64_t>(r_) * p.N;                          \
+          _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                    \
+            const f32x4_t v_ = acc[jn][im];                                                      \
+            const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                     \
+                                 (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);              \
+            const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                     \
+                                 (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);              \
+            *reinterpret_cast<u32x2_t*>(crow_ + jn * 16) = u32x2_t{lo_, hi_};                    \
+          }                                                                                      \
         }                                                                                        \
+      }                                                                                          \
+    } else {                                                                                     \
+      const int I_ = p.N / 2;                                                                    \
+      const int64_t ch0_ = static_cast<int64_t>(c_nt) * 128 + wn * CH + frag_k * 4;             \
+      constexpr int TH = TN / 2;                                                                 \
+      /* act of 4 channels of sub-tile pair (h, h + TH) of row block im, from the */           \
+      /* accumulators (read only: the result lives in a few temporaries)         */           \
+      auto act4_ = [&](int im, int h) -> f32x4_t {                                               \
+        f32x4_t r_;                                                                              \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                          \
+          const float gt_ = bf16_to_f32(f32_to_bf16(acc[h][im][e]));                             \
+          const float up_ = bf16_to_f32(f32_to_bf16(acc[h + TH][im][e]));                        \
+          r_[e] = bf16_to_f32(f32_to_bf16(silu_f32(gt_) * up_));                                 \
+        }                                                                                        \
+        return r_;                                                                               \
+      };                                                                                         \
+      if constexpr (EPI == kEpiSiluBf16) {                                                       \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
+          const int r_ = wm * WM + im * 16 + frag_row;                                           \
+          if (r_ < c_rows) {                                                                     \
+            uint16_t* const orow_ = static_cast<uint16_t*>(p.C) + (c_row0 + r_) * I_ + ch0_;     \
+            _Pragma("unroll") for (int h = 0; h < TH; ++h) {                                     \
+              const f32x4_t v_ = act4_(im, h);                                                   \
+              const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                   \
+                                   (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);            \
+              const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                   \
+                                   (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);            \
+              *reinterpret_cast<u32x2_t*>(orow_ + h * 16) = u32x2_t{lo_, hi_};                   \
+            }                                                                                    \
+          }                                                                                      \
+        }                                                                                        \
+      } else {                                                                                   \
+        /* Row maxima: over the lane's channels, the 4 lanes of the row       */                   \
+        /* (shuffles), then the column wavefronts (a small LDS array, one     */                   \
+        /* barrier); the activation is recomputed for the quantisation.       */                   \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
+          const int r_ = wm * WM + im * 16 + frag_row;                                           \
+          float m_ = 0.0f;                                                                       \
+          if (r_ < c_rows) {                                                                     \
+            _Pragma("unroll") for (int h = 0; h < TH; ++h) {                                     \
+              const f32x4_t v_ = act4_(im, h);                                                   \
+              _Pragma("unroll") for (int e = 0; e < 4; ++e) m_ = fmaxf(m_, fabsf(v_[e]));        \
+            }                                                                                    \
+          }                                                                                      \
+          m_ = fmaxf(m_, __shfl_xor(m_, 16, 64));                                                \
+          m_ = fmaxf(m_, __shfl_xor(m_, 32, 64));                                                \
+          if (frag_k == 0) lds_write_b32(rowmax + r_ * WAVES_N + wn, __float_as_uint(m_));       \
+        }                                                                                        \
+        __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): the maxima are in LDS */             \
+        __builtin_amdgcn_s_barrier();                                                            \
+        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                        \
+          _Pragma("unroll") for (int im = 0; im < TM; ++im) asm volatile("" : "+v"(acc[jn][im])); \
+        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
+          const int r_ = wm * WM + im * 16 + frag_row;                                           \
+          if (r_ < c_rows) {                                                                     \
+            float amax_ = 0.0f;                                                                  \
+            _Pragma("unroll") for (int w_ = 0; w_ < WAVES_N; w_ += 4) {                          \
+              const u32x4_t q4_ = lds_read_b128(rowmax + r_ * WAVES_N + w_);                     \
+              amax_ = fmaxf(amax_, fmaxf(fmaxf(__uint_as_float(q4_[0]), __uint_as_float(q4_[1])), \
+                                         fmaxf(__uint_as_float(q4_[2]), __uint_as_float(q4_[3])))); \
+            }                                                                                    \
+            const int ex_ = ue8m0_exponent(amax_);                                               \
+            uint8_t* const orow_ = static_cast<uint8_t*>(p.C) + (c_row0 + r_) * I_ + ch0_;       \
+            _Pragma("unroll") for (int h = 0; h < TH; ++h) {                                     \
+              const f32x4_t v_ = act4_(im, h);                                                   \
+              *reinterpret_cast<uint32_t*>(orow_ + h * 16) =                                     \
+                  e4m3x4(v_[0], v_[1], v_[2], v_[3], ex_);                                       \
+            }                                                                                    \
+            if (wn == 0 && frag_k == 0) {                                                        \
+              const int64_t si_ = MASKED                                                         \
+                  ? (static_cast<int64_t>(c_g) * (I_ / 128) + c_nt) * p.M + (c_row0 - static_cast<int64_t>(c_g) * p.M) + r_ \
+                  : static_cast<int64_t>(c_nt) * p.M + c_row0 + r_;                               \
+              p.C_scale[si_] = static_cast<uint8_t>(ex_ + 127);                                  \
+            }                                                                                    \
+          }                                                                                      \
+        }                                                                                        \
+        /* the maxima are rewritten only by the next tile's epilogue, after at */                \
+        /* least one step barrier                                               */               \
       }                                                                                          \
     }                                                                                            \
     _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                            \
@@ -553,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       MOE_EPILOGUE();                                                                            \
       c_epi = false;                                                                             \
       MOE_CSET(c_next);                                                                          \
-      c_next = next_tile(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);       \
+      c_next = next_tile<MASKED>(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);       \
     }                                                                                            \
     MOE_ISSUE(st);                                                                               \
     const int st1_ = st + 1 == kStages ? 0 : st + 1;                                             \
@@ -611,21 +773,22 @@ static int persistent_grid() {
   return grid[dev];
 }
 
-template <int BM, int BN, bool FP8, bool MASKED>
+template <int BM, int BN, bool FP8, bool MASKED, int EPI = kEpiPlain>
 int32_t launch_gemm(GemmArgs a, hipStream_t s) {
-  // The run table holds one XCD's share of the M-tiles and tile positions are
-  // 32-bit: bound the M-tiles of the order (compact: about a million rows).
+  // The compact run table holds one XCD's share of the M-tiles (about a
+  // million rows in all) and tile positions are 32-bit.
   const int64_t m_tiles = (a.M + BM - 1) / BM;
   const int64_t order_m = (MASKED ? a.G : 1) * m_tiles;
-  if (order_m > 8 * (kRunMax - 2)) return MOE_EUNSUPPORTED;
-  a.n_tiles = a.N / BN;
+  if (!MASKED && order_m > 8 * (kRunMax - 2)) return MOE_EUNSUPPORTED;
+  if (MASKED && a.G > kMaxMaskedGroups) return MOE_EUNSUPPORTED;
+  a.n_tiles = EPI == kEpiPlain ? a.N / BN : a.N / 256;
   a.m_tiles = static_cast<int>(m_tiles);
   const int64_t tiles = order_m * a.n_tiles;
   if (tiles == 0) return MOE_OK;
   if (tiles >= (1ll << 31)) return MOE_EUNSUPPORTED;
-  constexpr int lds = gemm_lds_bytes<BM, BN, FP8>();
+  constexpr int lds = gemm_lds_bytes<BM, BN, FP8, EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED>;
+  auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -669,7 +832,7 @@ extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8
   a.A_scale = A_scale;
   a.B = static_cast<const uint8_t*>(B);
   a.B_scale = B_scale;
-  a.C = static_cast<uint16_t*>(C);
+  a.C = C;
   a.rowinfo = m_indices;
   a.M = M;
   a.N = N;
@@ -696,7 +859,7 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   a.A_scale = A_scale;
   a.B = static_cast<const uint8_t*>(B);
   a.B_scale = B_scale;
-  a.C = static_cast<uint16_t*>(C);
+  a.C = C;
   a.rowinfo = masked_m;
   a.M = max_m;
   a.N = N;
@@ -712,4 +875,87 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   }
   if (n256) return fp8 ? launch_gemm<128, 256, true, true>(a, s) : launch_gemm<128, 256, false, true>(a, s);
   return fp8 ? launch_gemm<128, 128, true, true>(a, s) : launch_gemm<128, 128, false, true>(a, s);
+}
+
+// The w13 GEMM with SiLU-and-mul in its epilogue: B holds [G][2I][K] (gate
+// rows then up rows); out receives the activation [rows][I].
+static int32_t validate_silu(int32_t out_dtype, void* out, uint8_t* out_scale, int32_t I) {
+  if (I <= 0 || !out) return MOE_EINVAL;
+  if (I % 128 != 0) return MOE_EUNSUPPORTED;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
+  if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && !out_scale) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+extern "C" int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                            const void* B, const uint8_t* B_scale, int32_t out_dtype,
+                                            void* out, uint8_t* out_scale, const int32_t* m_indices,
+                                            int64_t M, int32_t I, int32_t K, int32_t G, void* stream) {
+  if (M < 0) return MOE_EINVAL;
+  int32_t st = validate_silu(out_dtype, out, out_scale, I);
+  if (st != MOE_OK) return st;
+  if (I > (1 << 29)) return MOE_EUNSUPPORTED;
+  st = validate_gemm(dtype, A, A_scale, B, B_scale, out, 2 * I, K, G);
+  if (st != MOE_OK) return st;
+  if (M == 0) return MOE_OK;
+  if (!m_indices) return MOE_EINVAL;
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.A_scale = A_scale;
+  a.B = static_cast<const uint8_t*>(B);
+  a.B_scale = B_scale;
+  a.C = out;
+  a.C_scale = out_scale;
+  a.rowinfo = m_indices;
+  a.M = M;
+  a.N = 2 * I;
+  a.K = K;
+  a.G = G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+    return fp8 ? launch_gemm<128, 256, true, false, kEpiSiluFp8>(a, s)
+               : launch_gemm<128, 256, false, false, kEpiSiluFp8>(a, s);
+  return fp8 ? launch_gemm<128, 256, true, false, kEpiSiluBf16>(a, s)
+             : launch_gemm<128, 256, false, false, kEpiSiluBf16>(a, s);
+}
+
+extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
+                                            const void* B, const uint8_t* B_scale, int32_t out_dtype,
+                                            void* out, uint8_t* out_scale, const int32_t* masked_m,
+                                            int32_t expected_m, int32_t max_m, int32_t I, int32_t K,
+                                            int32_t G, void* stream) {
+  if (max_m <= 0 || expected_m < 0) return MOE_EINVAL;
+  int32_t st = validate_silu(out_dtype, out, out_scale, I);
+  if (st != MOE_OK) return st;
+  if (I > (1 << 29)) return MOE_EUNSUPPORTED;
+  st = validate_gemm(dtype, A, A_scale, B, B_scale, out, 2 * I, K, G);
+  if (st != MOE_OK) return st;
+  if (!masked_m) return MOE_EINVAL;
+  if (G > kMaxMaskedGroups) return MOE_EUNSUPPORTED;
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.A_scale = A_scale;
+  a.B = static_cast<const uint8_t*>(B);
+  a.B_scale = B_scale;
+  a.C = out;
+  a.C_scale = out_scale;
+  a.rowinfo = masked_m;
+  a.M = max_m;
+  a.N = 2 * I;
+  a.K = K;
+  a.G = G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  const bool q8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if (expected_m > 0 && expected_m <= 64) {
+    if (q8) return fp8 ? launch_gemm<64, 256, true, true, kEpiSiluFp8>(a, s)
+                       : launch_gemm<64, 256, false, true, kEpiSiluFp8>(a, s);
+    return fp8 ? launch_gemm<64, 256, true, true, kEpiSiluBf16>(a, s)
+               : launch_gemm<64, 256, false, true, kEpiSiluBf16>(a, s);
+  }
+  if (q8) return fp8 ? launch_gemm<128, 256, true, true, kEpiSiluFp8>(a, s)
+                     : launch_gemm<128, 256, false, true, kEpiSiluFp8>(a, s);
+  return fp8 ? launch_gemm<128, 256, true, true, kEpiSiluBf16>(a, s)
+             : launch_gemm<128, 256, false, true, kEpiSiluBf16>(a, s);
 }

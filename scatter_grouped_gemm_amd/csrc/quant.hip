@@ -16,11 +16,8 @@ __device__ __forceinline__ uint2 quant8_group16(const float (&f)[8], int* e_out)
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = group_max<16>(amax);
   const int e = ue8m0_exponent(amax);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+  const uint32_t lo = e4m3x4(f[0], f[1], f[2], f[3], e);
+  const uint32_t hi = e4m3x4(f[4], f[5], f[6], f[7], e);
   *e_out = e;
   return make_uint2(lo, hi);
 }
@@ -63,43 +60,83 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   }
 }
 
-// One workgroup per 128x128 block; thread t covers rows 8*(t/16) .. +8 and
-// columns 8*(t%16) .. +8 of the block.
-__global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t* __restrict__ w, int N,
-                                                           int K, uint8_t* __restrict__ q,
-                                                           uint8_t* __restrict__ scale) {
-  __shared__ float wmax[4];
+// Weight blocks: one workgroup per 128x128 block; thread t covers rows
+// 8*(t/16) .. +8 and columns 8*(t%16) .. +8 of the block.  The block's bf16
+// values f (held by the threads) get one UE8M0 exponent from the block
+// maximum and are stored as e4m3.
+struct BlockPos {
+  int64_t g, blk;
+  int r0, c0;
+};
+__device__ __forceinline__ BlockPos block_pos(int N, int K) {
   const int nb = N / 128, kb = K / 128;
-  const int64_t blk = blockIdx.x;
-  const int64_t g = blk / (static_cast<int64_t>(nb) * kb);
-  const int bn = static_cast<int>((blk / kb) % nb), bk = static_cast<int>(blk % kb);
-  const int r0 = bn * 128 + (threadIdx.x >> 4) * 8;
-  const int c0 = bk * 128 + (threadIdx.x & 15) * 8;
-  const uint16_t* wg = w + g * N * static_cast<int64_t>(K);
-  float f[8][8];
+  BlockPos b;
+  b.blk = blockIdx.x;
+  b.g = b.blk / (static_cast<int64_t>(nb) * kb);
+  const int bn = static_cast<int>((b.blk / kb) % nb), bk = static_cast<int>(b.blk % kb);
+  b.r0 = bn * 128 + (threadIdx.x >> 4) * 8;
+  b.c0 = bk * 128 + (threadIdx.x & 15) * 8;
+  return b;
+}
+__device__ __forceinline__ void quant_block_store(const float (&f)[8][8], const BlockPos& b, int N,
+                                                  int K, uint8_t* __restrict__ q,
+                                                  uint8_t* __restrict__ scale) {
+  __shared__ float wmax[4];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    unpack8(*reinterpret_cast<const uint4*>(wg + static_cast<int64_t>(r0 + i) * K + c0), f[i]);
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[i][j]));
-  }
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int e = ue8m0_exponent(amax);
-  uint8_t* qg = q + g * N * static_cast<int64_t>(K);
+  uint8_t* qg = q + b.g * N * static_cast<int64_t>(K);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i][j], -e)) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i][4 + j], -e)) << (8 * j);
-    *reinterpret_cast<uint2*>(qg + static_cast<int64_t>(r0 + i) * K + c0) = make_uint2(lo, hi);
+    const uint32_t lo = e4m3x4(f[i][0], f[i][1], f[i][2], f[i][3], e);
+    const uint32_t hi = e4m3x4(f[i][4], f[i][5], f[i][6], f[i][7], e);
+    *reinterpret_cast<uint2*>(qg + static_cast<int64_t>(b.r0 + i) * K + b.c0) = make_uint2(lo, hi);
   }
-  if (threadIdx.x == 0) scale[blk] = static_cast<uint8_t>(e + 127);
+  if (threadIdx.x == 0) scale[b.blk] = static_cast<uint8_t>(e + 127);
+}
+
+__global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t* __restrict__ w, int N,
+                                                           int K, uint8_t* __restrict__ q,
+                                                           uint8_t* __restrict__ scale) {
+  const BlockPos b = block_pos(N, K);
+  const uint16_t* wg = w + b.g * N * static_cast<int64_t>(K);
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    unpack8(*reinterpret_cast<const uint4*>(wg + static_cast<int64_t>(b.r0 + i) * K + b.c0), f[i]);
+  quant_block_store(f, b, N, K, q, scale);
+}
+
+// Block-FP8 weights (e4m3 codes, one fp32 scale per 128x128 block) to the
+// UE8M0 block format: each element decode(q) * s in fp32, rounded to bf16,
+// then the block quantisation above.  q_out may be q_in: every thread reads
+// its 8x8 piece into registers before the block-wide barrier and writes the
+// same piece after it.
+__global__ __launch_bounds__(256) void requant_weight_kernel(const uint8_t* q_in,
+                                                             const float* __restrict__ s_in, int N,
+                                                             int K, uint8_t* q_out,
+                                                             uint8_t* __restrict__ s_out) {
+  const BlockPos b = block_pos(N, K);
+  const uint8_t* qg = q_in + b.g * N * static_cast<int64_t>(K);
+  const float sc = s_in[b.blk];
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint2 c = *reinterpret_cast<const uint2*>(qg + static_cast<int64_t>(b.r0 + i) * K + b.c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[i][j] = bf16_to_f32(f32_to_bf16(e4m3_to_f32((c.x >> (8 * j)) & 0xffu) * sc));
+      f[i][4 + j] = bf16_to_f32(f32_to_bf16(e4m3_to_f32((c.y >> (8 * j)) & 0xffu) * sc));
+    }
+  }
+  quant_block_store(f, b, N, K, q_out, s_out);
 }
 
 // SiLU-and-mul over one row per wavefront.  gate = first I columns, up = last I.
@@ -142,8 +179,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
       unpack8(uv[u], up);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float sv = gt[i] / (1.0f + expf(-gt[i]));
-        a[i] = bf16_to_f32(f32_to_bf16(sv * up[i]));  // the bf16 activation
+        a[i] = bf16_to_f32(f32_to_bf16(silu_f32(gt[i]) * up[i]));  // the bf16 activation
       }
       if (!FP8) {
         *reinterpret_cast<uint4*>(out + (r * I + col) * 2) = pack8(a);
@@ -190,6 +226,21 @@ extern "C" int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t 
   if (blocks >= (1ll << 31)) return MOE_EINVAL;
   quant_weight_kernel<<<static_cast<int>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint16_t*>(w), N, K, q, scale);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_requant_weight_fp8_ue8m0(const uint8_t* q_in, const float* s_in, int32_t G,
+                                                int32_t N, int32_t K, uint8_t* q_out,
+                                                uint8_t* s_out, void* stream) {
+  if (G < 0 || N <= 0 || K <= 0) return MOE_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (G == 0) return MOE_OK;
+  if (!q_in || !s_in || !q_out || !s_out) return MOE_EINVAL;
+  const int64_t blocks = static_cast<int64_t>(G) * (N / 128) * (K / 128);
+  if (blocks >= (1ll << 31)) return MOE_EINVAL;
+  requant_weight_kernel<<<static_cast<int>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      q_in, s_in, N, K, q_out, s_out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -237,11 +237,8 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
         }
         amax = group_max<16>(amax);
         const int e = ue8m0_exponent(amax);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+        const uint32_t lo = e4m3x4(f[0], f[1], f[2], f[3], e);
+        const uint32_t hi = e4m3x4(f[4], f[5], f[6], f[7], e);
         const uint2 q = make_uint2(lo, hi);
         const bool leader = (threadIdx.x & 15) == 0;
         for (int j = 0; j < k; ++j) {

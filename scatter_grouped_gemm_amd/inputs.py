@@ -166,6 +166,18 @@ def small_case(seed: int, T: int, H: int, I: int, E: int, k: int, *, El=None,
     return x, L, w13, w2
 
 
+def block_fp8_checkpoint(G: int, N: int, K: int, seed: int, device="cpu"):
+    """Synthetic block-FP8 expert weights as a checkpoint stores them: e4m3
+    codes [G,N,K] (uint8, bell-shaped over the code range, no NaN codes) and one
+    positive fp32 scale per 128x128 block [G,N/128,K/128], log-uniform over
+    2^-14 .. 2^-4 and not powers of two."""
+    g = torch.Generator().manual_seed(seed)
+    v = (torch.randn(G, N, K, generator=g) * 96.0).clamp_(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = torch.exp2(torch.rand(G, N // 128, K // 128, generator=g) * 10.0 - 14.0)
+    return codes.to(device), scales.to(device)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor as a numpy uint16 array (on the host)."""
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
@@ -183,5 +195,5 @@ def zipf_reference_shares(E_live: int, s: float = 1.2) -> np.ndarray:
 
 
 __all__ = ["Workload", "WORKLOADS", "ALIASES", "get", "tokens", "logits", "expert_bias",
-           "expert_weights", "local_weights", "small_case", "bf16_bits", "from_bf16_bits",
+           "expert_weights", "local_weights", "small_case", "block_fp8_checkpoint", "bf16_bits", "from_bf16_bits",
            "zipf_reference_shares"]

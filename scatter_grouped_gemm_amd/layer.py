@@ -24,7 +24,8 @@ class MoELayer:
     def __init__(self, *, hidden: int, intermediate: int, num_experts: int, top_k: int,
                  max_tokens: int, num_local_experts: int | None = None, expert_start: int = 0,
                  fp8: bool = False, layout: str = "auto", block_e: int = 128,
-                 max_m: int | None = None, expected_m: int = 0, device="cuda"):
+                 max_m: int | None = None, expected_m: int = 0, fuse_silu: bool = True,
+                 device="cuda"):
         self.H, self.I, self.E, self.k = hidden, intermediate, num_experts, top_k
         self.El = num_local_experts or num_experts
         self.expert_start = expert_start
@@ -37,6 +38,8 @@ class MoELayer:
         if layout not in ("compact", "masked"):
             raise ValueError(f"unknown layout {layout!r}")
         self.layout = layout
+        # w13 with SiLU-and-mul in its epilogue (bit-identical to the two calls)
+        self.fuse_silu = fuse_silu
         self.max_m = max_m if max_m is not None else max_tokens
         self.expected_m = expected_m
         d, T, H, I, El, k = self.device, max_tokens, hidden, intermediate, self.El, top_k
@@ -52,7 +55,7 @@ class MoELayer:
         self.src2dst = torch.empty(T, k, dtype=torch.int32, device=d)
         self.x_buf = torch.empty(R, H, dtype=adt, device=d)
         self.x_scale = torch.empty(R * (H // 128), dtype=torch.uint8, device=d) if fp8 else None
-        self.gateup = torch.empty(R, 2 * I, dtype=torch.bfloat16, device=d)
+        self.gateup = None if fuse_silu else torch.empty(R, 2 * I, dtype=torch.bfloat16, device=d)
         self.act = torch.empty(R, I, dtype=adt, device=d)
         self.act_scale = torch.empty(R * (I // 128), dtype=torch.uint8, device=d) if fp8 else None
         self.y = torch.empty(R, H, dtype=torch.bfloat16, device=d)
@@ -104,6 +107,18 @@ class MoELayer:
         for e in range(self.El):
             self.set_expert(e, w13[e], w2[e])
 
+    def set_block_fp8_weights(self, w13q, w13s, w2q, w2s):
+        """Take block-FP8 checkpoint weights (e4m3 bytes, one fp32 scale per
+        128x128 block: w13 [El,2I,H] + [El,2I/128,H/128], w2 [El,H,I] +
+        [El,H/128,I/128]) and requantise them in the library to UE8M0 scales
+        through bf16."""
+        if not self.fp8:
+            raise ValueError("block-FP8 weights given to a BF16 layer: the activation dtype follows the weights")
+        if self.w13 is None:
+            self.allocate_weights()
+        L.moe_requant_weight_fp8_ue8m0(w13q.contiguous(), w13s.contiguous(), self.w13, self.w13_scale)
+        L.moe_requant_weight_fp8_ue8m0(w2q.contiguous(), w2s.contiguous(), self.w2, self.w2_scale)
+
     def set_quantized_weights(self, w13q, w13s, w2q, w2s):
         """Take already block-quantised FP8 weights (e4m3 bytes + UE8M0 bytes)."""
         if not self.fp8:
@@ -135,11 +150,16 @@ class MoELayer:
                 L.moe_scatter_compact(x, ids, self.expert_start, self.El, self.block_e, self.rows,
                                       fp8, self.x_buf, self.x_scale, self.m_indices,
                                       self.expert_start_loc, self.num_valid, s2d, self.ws)
-            with self._mark("gemm_w13"):
-                L.grouped_gemm_contig(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
-                                      self.gateup, self.m_indices)
-            with self._mark("silu_and_mul"):
-                L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, m_indices=self.m_indices)
+            if self.fuse_silu:
+                with self._mark("gemm_w13_silu"):
+                    L.grouped_gemm_contig_silu(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
+                                               self.act, self.m_indices, self.act_scale)
+            else:
+                with self._mark("gemm_w13"):
+                    L.grouped_gemm_contig(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
+                                          self.gateup, self.m_indices)
+                with self._mark("silu_and_mul"):
+                    L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, m_indices=self.m_indices)
             with self._mark("gemm_w2"):
                 L.grouped_gemm_contig(fp8, self.act, self.act_scale, self.w2, self.w2_scale, self.y,
                                       self.m_indices)
@@ -148,13 +168,19 @@ class MoELayer:
             with self._mark("scatter"):
                 L.moe_scatter_masked(x, ids, self.expert_start, El, mm, fp8, self.x_buf,
                                      self.x_scale, self.masked_m, s2d, self.ws)
-            with self._mark("gemm_w13"):
-                L.grouped_gemm_masked(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
-                                      self.w13, self.w13_scale, self.gateup.view(El, mm, 2 * I),
-                                      self.masked_m, self.expected_m)
-            with self._mark("silu_and_mul"):
-                L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, masked_m=self.masked_m,
-                               max_m=mm)
+            if self.fuse_silu:
+                with self._mark("gemm_w13_silu"):
+                    L.grouped_gemm_masked_silu(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
+                                               self.w13, self.w13_scale, self.act.view(El, mm, I),
+                                               self.masked_m, self.expected_m, self.act_scale)
+            else:
+                with self._mark("gemm_w13"):
+                    L.grouped_gemm_masked(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
+                                          self.w13, self.w13_scale, self.gateup.view(El, mm, 2 * I),
+                                          self.masked_m, self.expected_m)
+                with self._mark("silu_and_mul"):
+                    L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, masked_m=self.masked_m,
+                                   max_m=mm)
             with self._mark("gemm_w2"):
                 L.grouped_gemm_masked(fp8, self.act.view(El, mm, I), self.act_scale, self.w2,
                                       self.w2_scale, self.y.view(El, mm, self.H), self.masked_m,

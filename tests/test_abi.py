@@ -83,6 +83,10 @@ def test_validation_rejects_before_launch():
     assert lib.moe_quant_fp8_ue8m0(P, 4, 100, 100, None, P, P, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_quant_fp8_ue8m0(P, 4, 128, 64, None, P, P, None) == L.MOE_EINVAL
     assert lib.moe_quant_weight_fp8_ue8m0(P, 2, 128, 96, P, P, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_requant_weight_fp8_ue8m0(P, P, 2, 128, 96, P, P, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_requant_weight_fp8_ue8m0(P, P, -1, 128, 128, P, P, None) == L.MOE_EINVAL
+    assert lib.moe_requant_weight_fp8_ue8m0(P, None, 2, 128, 128, P, P, None) == L.MOE_EINVAL
+    assert lib.moe_requant_weight_fp8_ue8m0(None, None, 0, 128, 128, None, None, None) == L.MOE_OK
     # grouped GEMMs: dtype follows the weights -> FP8 without scales is an error
     assert lib.grouped_gemm_contig(1, P, None, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
     assert lib.grouped_gemm_contig(1, P, P, P, None, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
@@ -100,9 +104,18 @@ def test_validation_rejects_before_launch():
     assert lib.silu_and_mul(P, 15, 128, None, P, 8, 0, P, None, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 33, 256, P, None) == L.MOE_EINVAL
     assert lib.moe_combine(P, 10, P, P, 4, 2, 100, P, None) == L.MOE_EUNSUPPORTED
-    # the on-chip run table bounds the M-tiles of the tile order
+    # the on-chip run table bounds the M-tiles of the compact tile order, and
+    # tile positions are 32-bit
     assert lib.grouped_gemm_contig(0, P, None, P, None, P, P, 8177 * 128, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
-    assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 0, 4096, 256, 256, 256, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 0, 1 << 30, 256, 256, 1024, None) == L.MOE_EUNSUPPORTED
+    # w13 with SiLU-and-mul fused
+    assert lib.grouped_gemm_contig_silu(0, P, None, P, None, 0, P, None, P, 256, 100, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig_silu(0, P, None, P, None, 7, P, None, P, 256, 128, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig_silu(0, P, None, P, None, 1, P, None, P, 256, 128, 256, 2, None) == L.MOE_EINVAL
+    assert lib.grouped_gemm_contig_silu(1, P, None, P, P, 0, P, None, P, 256, 128, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig_silu(0, P, None, P, None, 0, P, None, None, 256, 128, 256, 2, None) == L.MOE_EINVAL
+    assert lib.grouped_gemm_masked_silu(0, P, None, P, None, 0, P, None, P, 0, 64, 128, 256, 1025, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_masked_silu(0, P, None, P, None, 0, P, None, P, 0, 0, 128, 256, 2, None) == L.MOE_EINVAL
     # masked tile prefix is held on chip for at most 1024 groups
     assert lib.grouped_gemm_masked(0, P, None, P, None, P, P, 8, 64, 256, 256, 1025, None) == L.MOE_EUNSUPPORTED
 
@@ -113,4 +126,6 @@ def test_empty_calls_are_no_ops():
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == L.MOE_OK
     assert lib.moe_quant_fp8_ue8m0(None, 0, 128, 128, None, None, None, None) == L.MOE_OK
     assert lib.grouped_gemm_contig(0, FAKE, None, FAKE, None, FAKE, None, 0, 256, 256, 2, None) == L.MOE_OK
+    assert lib.grouped_gemm_contig_silu(0, FAKE, None, FAKE, None, 0, FAKE, None, None, 0, 128, 256, 2,
+                                        None) == L.MOE_OK
     assert lib.moe_combine(None, 0, None, None, 0, 2, 256, None, None) == L.MOE_OK

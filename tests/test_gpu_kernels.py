@@ -210,6 +210,57 @@ def test_quant_weight_blocks(orc):
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def _requant_inputs():
+    q, s = inputs.block_fp8_checkpoint(3, 256, 384, seed=11)
+    q[1, :128, :128] = 0                      # zero block (both signs of zero)
+    q[1, :64, :128] = 0x80
+    q[1, 128:, 128:256] &= 0x87               # subnormal codes only
+    q[2, :128, 256:] = 0x7e                   # every element at the e4m3 maximum
+    s[1, 0, 2] = 2.0 ** 100                   # bf16 near its top of range
+    s[2, 1, 0] = 2.0 ** -126                  # products in the fp32 subnormal range
+    s[2, 1, 1] = 1.0
+    return q, s
+
+
+def test_requant_weight_blocks(orc):
+    announce("requant_weight_fp8_ue8m0")
+    q_in, s_in = _requant_inputs()
+    q_ref, s_ref = orc.requant_weight_blocks(q_in.numpy(), s_in.numpy())
+    q = poison((3, 256, 384), torch.uint8)
+    s = poison((3, 2, 3), torch.uint8)
+    L.moe_requant_weight_fp8_ue8m0(q_in.to(DEV), s_in.to(DEV), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_requant_weight_blocks_in_place(orc):
+    announce("requant_weight_fp8_ue8m0 in place")
+    q_in, s_in = _requant_inputs()
+    q_ref, s_ref = orc.requant_weight_blocks(q_in.numpy(), s_in.numpy())
+    q = q_in.to(DEV)
+    s = poison((3, 2, 3), torch.uint8)
+    L.moe_requant_weight_fp8_ue8m0(q, s_in.to(DEV), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_requant_then_gemm_matches_dequantised_weights(orc):
+    """The requantised weights drive the FP8 GEMM like weights quantised from
+    their bf16 dequantisation (the two give identical codes and scales)."""
+    announce("requant_weight_fp8_ue8m0 vs quant_weight of the dequantised bf16")
+    q_in, s_in = inputs.block_fp8_checkpoint(2, 256, 512, seed=12)
+    deq = (q_in.view(torch.float8_e4m3fn).float()
+           * s_in.repeat_interleave(128, 1).repeat_interleave(128, 2)).to(torch.bfloat16)
+    q1, s1 = poison((2, 256, 512), torch.uint8), poison((2, 2, 4), torch.uint8)
+    q2, s2 = poison((2, 256, 512), torch.uint8), poison((2, 2, 4), torch.uint8)
+    L.moe_requant_weight_fp8_ue8m0(q_in.to(DEV), s_in.to(DEV), q1, s1)
+    L.moe_quant_weight_fp8_ue8m0(deq.to(DEV), q2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
 # ---------------------------------------------------------------------------
 # grouped GEMMs
 # ---------------------------------------------------------------------------
@@ -400,6 +451,114 @@ def test_gemm_masked_many_groups(orc, fp8):
     valid = rg >= 0
     assert np.array_equal(got[valid], ref[valid])
     assert np.all(got[_skipped_rows_masked(masked, max_m)] == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("expected_m", [0, 8])
+def test_gemm_masked_max_groups_long_tail(orc, fp8, expected_m):
+    """1024 groups (the maximum), most short, some spanning up to ten tiles,
+    the last group full: tiles are found through the group prefix for every
+    position of the order (with 64-row tiles the order has 10240 M-tiles)."""
+    announce("gemm_masked_max_groups", fp8, expected_m)
+    G, max_m, N, K = 1024, 640, 128, 128
+    rng = np.random.default_rng(5)
+    masked = rng.integers(0, 21, G).astype(np.int32)
+    for g, m in ((3, 640), (4, 129), (5, 128), (6, 64), (7, 65), (500, 513), (1022, 0), (1023, 640)):
+        masked[g] = m
+    ops = _gemm_operands(orc, fp8, [max_m] * G, N, K, seed=17, integer_valued=True)
+    rg = orc.masked_row_group(masked, max_m)
+    A = ops["A"][: G * max_m]
+    C = poison((G, max_m, N), torch.bfloat16)
+    if fp8:
+        ref = orc.gemm_fp8_rows(A, ops["As"][: G * max_m], ops["B"], ops["Bs"], rg)
+        As = ops["As"][: G * max_m].reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
+        L.grouped_gemm_masked(True, u8_dev(A).view(G, max_m, K), u8_dev(As), u8_dev(ops["B"]),
+                              u8_dev(ops["Bs"]), C, i32_dev(masked), expected_m)
+    else:
+        ref = orc.gemm_bf16_rows(A, ops["B"], rg)
+        L.grouped_gemm_masked(False, to_dev_bf16(A).view(G, max_m, K), None, to_dev_bf16(ops["B"]),
+                              None, C, i32_dev(masked), expected_m)
+    torch.cuda.synchronize()
+    got = bits(C).reshape(G * max_m, N)
+    valid = rg >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[_skipped_rows_masked(masked, max_m)] == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("out_fp8", [False, True])
+def test_gemm_silu_fused_contig(orc, fp8, out_fp8):
+    """w13 with SiLU-and-mul in the epilogue equals grouped_gemm_contig
+    followed by silu_and_mul bit for bit on every valid row (activation and,
+    for FP8 output, the UE8M0 scales)."""
+    announce("gemm_silu_contig", fp8, out_fp8)
+    I, K = 256, 384
+    ops = _gemm_operands(orc, fp8, [130, 0, 5, 256, 1, 300], 2 * I, K, seed=21)
+    M = len(ops["m_idx"])
+    m_dev = i32_dev(ops["m_idx"])
+    if fp8:
+        A, As = u8_dev(ops["A"]), u8_dev(ops["As"].T.copy())
+        B, Bs = u8_dev(ops["B"]), u8_dev(ops["Bs"])
+    else:
+        A, As, B, Bs = to_dev_bf16(ops["A"]), None, to_dev_bf16(ops["B"]), None
+    C = poison((M, 2 * I), torch.bfloat16)
+    L.grouped_gemm_contig(fp8, A, As, B, Bs, C, m_dev)
+    odt = torch.uint8 if out_fp8 else torch.bfloat16
+    sep = poison((M, I), odt)
+    sep_s = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    L.silu_and_mul(C, sep, out_fp8, sep_s, m_indices=m_dev)
+    fused = poison((M, I), odt)
+    fused_s = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    L.grouped_gemm_contig_silu(fp8, A, As, B, Bs, fused, m_dev, fused_s)
+    torch.cuda.synchronize()
+    v = ops["m_idx"] >= 0
+    a, b = fused.cpu(), sep.cpu()
+    if not out_fp8:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    assert torch.equal(a[torch.from_numpy(v)], b[torch.from_numpy(v)])
+    if out_fp8:
+        assert np.array_equal(fused_s.cpu().numpy()[:, v], sep_s.cpu().numpy()[:, v])
+    skipped = _skipped_rows_contig(ops["m_idx"])
+    untouched = 0xFF if out_fp8 else -1
+    assert bool((fused.cpu().view(torch.uint8 if out_fp8 else torch.int16)[torch.from_numpy(skipped)] == untouched).all())
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("out_fp8", [False, True])
+@pytest.mark.parametrize("expected_m", [0, 8])
+def test_gemm_silu_fused_masked(orc, fp8, out_fp8, expected_m):
+    """Masked layout, both tile heights: fused equals separate bit for bit."""
+    announce("gemm_silu_masked", fp8, out_fp8, expected_m)
+    G, max_m, I, K = 5, 200, 256, 256
+    masked = np.array([0, 1, 200, 37, 130], np.int32)
+    ops = _gemm_operands(orc, fp8, [max_m] * G, 2 * I, K, seed=23)
+    A = ops["A"][: G * max_m]
+    if fp8:
+        As = ops["As"][: G * max_m].reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
+        Ad, Asd, B, Bs = u8_dev(A).view(G, max_m, K), u8_dev(As), u8_dev(ops["B"]), u8_dev(ops["Bs"])
+    else:
+        Ad, Asd, B, Bs = to_dev_bf16(A).view(G, max_m, K), None, to_dev_bf16(ops["B"]), None
+    mm = i32_dev(masked)
+    C = poison((G, max_m, 2 * I), torch.bfloat16)
+    L.grouped_gemm_masked(fp8, Ad, Asd, B, Bs, C, mm, expected_m)
+    odt = torch.uint8 if out_fp8 else torch.bfloat16
+    sep = poison((G * max_m, I), odt)
+    sep_s = poison((G, I // 128, max_m), torch.uint8) if out_fp8 else None
+    L.silu_and_mul(C.view(G * max_m, 2 * I), sep, out_fp8, sep_s, masked_m=mm, max_m=max_m)
+    fused = poison((G, max_m, I), odt)
+    fused_s = poison((G, I // 128, max_m), torch.uint8) if out_fp8 else None
+    L.grouped_gemm_masked_silu(fp8, Ad, Asd, B, Bs, fused, mm, expected_m, fused_s)
+    torch.cuda.synchronize()
+    rg = orc.masked_row_group(masked, max_m)
+    v = torch.from_numpy(rg >= 0)
+    a, b = fused.cpu().view(G * max_m, I), sep.cpu()
+    if not out_fp8:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    assert torch.equal(a[v], b[v])
+    if out_fp8:
+        fs, ss = fused_s.cpu().numpy(), sep_s.cpu().numpy()
+        for g in range(G):
+            assert np.array_equal(fs[g, :, : masked[g]], ss[g, :, : masked[g]])
 
 
 # ---------------------------------------------------------------------------

@@ -2,6 +2,8 @@
 the invariances the pages ask for: masked and compact layouts agree, a token's
 output bits do not depend on its batch, and uninitialised (poisoned) buffers
 do not leak into results."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -47,7 +49,7 @@ CASES = [
 @pytest.mark.parametrize("name,T,H,I,E,El,start,k,fp8,layout", CASES)
 def test_layer_matches_oracle(orc, name, T, H, I, E, El, start, k, fp8, layout):
     announce("layer", name)
-    x, logits, w13, w2 = inputs.small_case(hash(name) % 1000, T, H, I, E, k, El=El or E)
+    x, logits, w13, w2 = inputs.small_case(zlib.crc32(name.encode()) % 1000, T, H, I, E, k, El=El or E)
     layer = _layer(T, H, I, E, k, El=El, start=start, fp8=fp8, layout=layout,
                    expected_m=max(1, T * k // E))
     layer.set_weights(w13.to(DEV), w2.to(DEV))
@@ -131,8 +133,50 @@ def test_uninitialised_buffers_do_not_leak(fp8):
     assert np.array_equal(res[0], res[1]) and np.array_equal(res[0], res[2])
 
 
+@pytest.mark.parametrize("layout", ["compact", "masked"])
+def test_layer_block_fp8_checkpoint(orc, layout):
+    """Block-FP8 checkpoint weights requantised in the library drive the layer
+    like the oracle's requantisation of the same codes and scales."""
+    announce("layer_block_fp8_checkpoint", layout)
+    T, H, I, E, k = 160, 256, 384, 16, 4
+    x, logits, _, _ = inputs.small_case(77, T, H, I, E, k)
+    w13q, w13s = inputs.block_fp8_checkpoint(E, 2 * I, H, seed=78)
+    w2q, w2s = inputs.block_fp8_checkpoint(E, H, I, seed=79)
+    layer = _layer(T, H, I, E, k, fp8=True, layout=layout, expected_m=T * k // E)
+    layer.set_block_fp8_weights(w13q.to(DEV), w13s.to(DEV), w2q.to(DEV), w2s.to(DEV))
+    out = layer(x.to(DEV), logits.to(DEV))
+    torch.cuda.synchronize()
+    a, b = orc.requant_weight_blocks(w13q.numpy(), w13s.numpy())
+    c, d = orc.requant_weight_blocks(w2q.numpy(), w2s.numpy())
+    assert np.array_equal(layer.w13.cpu().numpy(), a) and np.array_equal(layer.w13_scale.cpu().numpy(), b)
+    assert np.array_equal(layer.w2.cpu().numpy(), c) and np.array_equal(layer.w2_scale.cpu().numpy(), d)
+    ref = orc.moe_layer(bits(x), logits.numpy(), k, expert_start=0, num_local_experts=E,
+                        layout=layout, fp8=True, max_m=T, w13q=a, w13s=b, w2q=c, w2s=d)
+    err = rel_fro(f32(bits(out)).astype(np.float64), f32(ref["out"]))
+    assert err <= 2e-2, err
+
+
 def test_fp8_layer_rejects_bf16_mix():
     announce("dtype_follows_weights")
     layer = _layer(8, 128, 128, 4, 2, fp8=False)
     with pytest.raises(ValueError):
         layer.set_quantized_weights(None, None, None, None)
+    with pytest.raises(ValueError):
+        layer.set_block_fp8_weights(None, None, None, None)
+
+
+@pytest.mark.parametrize("name,T,H,I,E,El,start,k,fp8,layout", CASES)
+def test_layer_fused_silu_matches_unfused(name, T, H, I, E, El, start, k, fp8, layout):
+    """SiLU-and-mul fused into the w13 GEMM gives the same output bits as the
+    two separate kernels."""
+    announce("layer_fused", name)
+    x, logits, w13, w2 = inputs.small_case(zlib.crc32(name.encode()) % 1000, T, H, I, E, k, El=El or E)
+    outs = []
+    for fuse in (True, False):
+        layer = MoELayer(hidden=H, intermediate=I, num_experts=E, top_k=k, max_tokens=T,
+                         num_local_experts=El, expert_start=start, fp8=fp8, layout=layout,
+                         expected_m=max(1, T * k // E), fuse_silu=fuse, device=DEV)
+        layer.set_weights(w13.to(DEV), w2.to(DEV))
+        outs.append(bits(layer(x.to(DEV), logits.to(DEV))))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
