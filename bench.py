@@ -123,6 +123,37 @@ def measured_traffic(wl_name, which):
     return int(d[which]["read_bytes"] + d[which]["write_bytes"])
 
 
+def requant_weights(wl, torch, reps=5):
+    """Time moe_requant_weight_fp8_ue8m0 on block-FP8 checkpoint weights of the
+    workload's w13 shape (seeded random e4m3 codes without NaN, fp32 block
+    scales log-uniform over 2^-14 .. 2^-4): a load-time step, outside the
+    timed path.  Algorithmic bytes: each code read and written once, plus
+    4 + 1 scale bytes per 128x128 block."""
+    from scatter_grouped_gemm_amd import _lib as L
+    G, N, K = wl.El, 2 * wl.I, wl.H
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    q = torch.randint(0, 0x7F, (G, N, K), dtype=torch.uint8, device="cuda", generator=g)
+    q |= torch.randint(0, 2, (G, N, K), dtype=torch.uint8, device="cuda", generator=g) << 7
+    s_in = torch.exp2(torch.rand(G, N // 128, K // 128, device="cuda", generator=g) * 10.0 - 14.0)
+    q_out = torch.empty_like(q)
+    s_out = torch.empty(G, N // 128, K // 128, dtype=torch.uint8, device="cuda")
+    L.moe_requant_weight_fp8_ue8m0(q, s_in, q_out, s_out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        L.moe_requant_weight_fp8_ue8m0(q, s_in, q_out, s_out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 2 * G * N * K + 5 * G * (N // 128) * (K // 128)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, q_out, s_in, s_out
+    return dict(shape=[G, N, K], ms=round(ms, 4), achieved=round(gbs, 1), peak=PEAK_HBM_GBS,
+                unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
+
+
 def cpu_baseline(wl, x, logits, target_s, torch):
     """The oracle, as it stands, on a prefix of the same batch: routing plus the
     layout-free per-token expert path (w13 -> SiLU-mul -> (requant) -> w2 ->
@@ -259,6 +290,10 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "cpu_baseline": None,
     }
+    if wl.fp8:
+        res["requant_weights"] = requant_weights(wl, torch)
+        log(f"requant of w13-shaped block-FP8 weights: {res['requant_weights']['ms']:.3f} ms, "
+            f"{res['requant_weights']['achieved']:.0f} GB/s")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
     print(json.dumps(res), flush=True)

@@ -71,6 +71,17 @@ int64_t moe_compact_rows_bound(int64_t num_assignments, int32_t num_local_expert
  * else 0 (compact). */
 int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_experts);
 
+/* Layout policy measured on MI355X in place of the rule above, which the pages
+ * leave open ("Support DeepGEMM for standard MoE dispatch", comments section:
+ * compact slower than masked up to a crossover in token count).  Timing the
+ * whole path in both layouts over 16 .. 16384 tokens (DeepSeek-V3 and two BF16
+ * shapes, 8 .. 256 local experts) put the masked layout 4-23% ahead up to 1024
+ * tokens and within 2% of compact from 4096, where its E_local * T rows cost
+ * far more memory.  Returns 1 (masked) when max_tokens <= 2048 and
+ * max_tokens * num_local_experts <= 2^20 rows, else 0; -1 for a negative or
+ * zero argument. */
+int32_t moe_choose_layout(int64_t max_tokens, int32_t num_local_experts);
+
 /* Scratch bytes moe_scatter_compact / moe_scatter_masked need for T tokens,
  * top-k and num_local_experts local experts. */
 size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts);

@@ -61,6 +61,11 @@ def _load():
         "orc_quant_rows": (None, [P, i64, i32, i64, P, P]),
         "orc_quant_weight_blocks": (None, [P, i32, i32, i32, P, P]),
         "orc_requant_weight_blocks": (None, [P, P, i32, i32, i32, P, P]),
+        "orc_e2m1_to_f64": (f64, [ctypes.c_uint8]),
+        "orc_e2m1_from_f64": (ctypes.c_uint8, [f64]),
+        "orc_mx_exponent": (i32, [f64, f64]),
+        "orc_quant_weight_mx": (None, [P, i32, i32, i32, i32, P, P]),
+        "orc_gemm_mx_rows": (None, [P, P, i64, P, P, i32, i32, i32, P, P]),
         "orc_scatter_compact": (i32, [P, i32, i32, P, i32, i32, i32, i32, i64, i32,
                                       P, P, P, P, P, P]),
         "orc_scatter_masked": (i32, [P, i32, i32, P, i32, i32, i32, i32, i32,
@@ -252,6 +257,51 @@ def gemm_fp8_rows(A, A_scale, B, B_scale, row_group):
     return C
 
 
+MX_FORMATS = {"mxfp8": 0, "mxfp4": 1}
+
+
+def e2m1_to_f64(q: int) -> float:
+    return float(_load().orc_e2m1_to_f64(int(q)))
+
+
+def e2m1_from_f64(v: float) -> int:
+    return int(_load().orc_e2m1_from_f64(float(v)))
+
+
+def mx_exponent(amax: float, fmax: float) -> int:
+    return int(_load().orc_mx_exponent(float(amax), float(fmax)))
+
+
+def quant_weight_mx(w: np.ndarray, fmt: str):
+    """MX weights from bf16 w[G,N,K]: (codes, scales [G,N,K/32]); codes are e4m3
+    [G,N,K] for "mxfp8", e2m1 two per byte [G,N,K/2] (even k low) for "mxfp4"."""
+    w = _c(w, np.uint16)
+    G, N, K = w.shape
+    assert K % 32 == 0
+    f = MX_FORMATS[fmt]
+    q = np.zeros((G, N, K if f == 0 else K // 2), np.uint8)
+    sc = np.empty((G, N, K // 32), np.uint8)
+    _load().orc_quant_weight_mx(_p(w), G, N, K, f, _p(q), _p(sc))
+    return q, sc
+
+
+def gemm_mx_rows(A, A_scale, B, B_scale, fmt: str, row_group):
+    """FP8 rows (scales [M, K/128]) times MX weights of format fmt."""
+    A = _c(A, np.uint8)
+    As = _c(A_scale, np.uint8)
+    B = _c(B, np.uint8)
+    Bs = _c(B_scale, np.uint8)
+    rg = _c(row_group, np.int32)
+    f = MX_FORMATS[fmt]
+    M, K = A.shape
+    G, N, Kb = B.shape
+    assert Kb == (K if f == 0 else K // 2) and As.shape == (M, K // 128)
+    assert Bs.shape == (G, N, K // 32) and rg.shape[0] == M
+    C = np.zeros((M, N), np.uint16)
+    _load().orc_gemm_mx_rows(_p(A), _p(As), M, _p(B), _p(Bs), f, N, K, _p(rg), _p(C))
+    return C
+
+
 def silu_and_mul(gateup, row_group):
     gu = _c(gateup, np.uint16)
     rg = _c(row_group, np.int32)
@@ -299,9 +349,11 @@ def moe_dense(x, topk_ids, topk_weights, expert_start, num_local_experts, fp8,
 
 def moe_layer(x, logits, k, *, expert_start, num_local_experts, layout, fp8,
               block_e=128, rows_capacity=None, max_m=None,
-              w13=None, w2=None, w13q=None, w13s=None, w2q=None, w2s=None):
+              w13=None, w2=None, w13q=None, w13s=None, w2q=None, w2s=None, mx=None):
     """The layout path step by step: route -> scatter -> w13 -> SiLU-mul ->
-    (requantise) -> w2 -> combine.  Returns the output and every intermediate."""
+    (requantise) -> w2 -> combine.  Returns the output and every intermediate.
+    mx = "mxfp8" / "mxfp4": the FP8 path with MX weights (w13q/w13s and
+    w2q/w2s from quant_weight_mx)."""
     ids, tw = route_topk(logits, k)
     T = x.shape[0]
     if layout == "compact":
@@ -313,8 +365,16 @@ def moe_layer(x, logits, k, *, expert_start, num_local_experts, layout, fp8,
     else:
         sc = scatter_masked(x, ids, expert_start, num_local_experts, max_m, fp8)
         rg = masked_row_group(sc["masked_m"], max_m)
+    if mx is not None:
+        assert fp8
+
+    def wgemm(a, a_s, q, s_):
+        if mx is not None:
+            return gemm_mx_rows(a, a_s, q, s_, mx, rg)
+        return gemm_fp8_rows(a, a_s, q, s_, rg)
+
     if fp8:
-        h1 = gemm_fp8_rows(sc["x_out"], sc["scale_out"], w13q, w13s, rg)
+        h1 = wgemm(sc["x_out"], sc["scale_out"], w13q, w13s)
         act = silu_and_mul(h1, rg)
         aq = np.zeros(act.shape, np.uint8)
         asc = np.zeros((act.shape[0], act.shape[1] // 128), np.uint8)
@@ -322,7 +382,7 @@ def moe_layer(x, logits, k, *, expert_start, num_local_experts, layout, fp8,
         if valid.any():
             q, s = quant_rows(act[valid])
             aq[valid], asc[valid] = q, s
-        y = gemm_fp8_rows(aq, asc, w2q, w2s, rg)
+        y = wgemm(aq, asc, w2q, w2s)
     else:
         h1 = gemm_bf16_rows(sc["x_out"], w13, rg)
         act = silu_and_mul(h1, rg)

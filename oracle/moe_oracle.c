@@ -244,6 +244,82 @@ void orc_requant_weight_blocks(const uint8_t* q_in, const float* s_in, int32_t G
 }
 
 /* ------------------------------------------------------------------------ */
+/* MX expert weights (microscaling: one power-of-two scale per 32 values)     */
+/* ------------------------------------------------------------------------ */
+
+/* OCP microscaling FP4 element, e2m1: sign bit 3, two exponent bits (bias 1),
+ * one mantissa bit; exponent field 0 holds 0 and 0.5, otherwise the value is
+ * 2^(E-1) * (1 + M/2).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or NaN. */
+double orc_e2m1_to_f64(uint8_t q) {
+  int s = (q >> 3) & 1, ef = (q >> 1) & 3, mf = q & 1;
+  double v = ef == 0 ? 0.5 * mf : ldexp(1.0 + 0.5 * mf, ef - 1);
+  return s ? -v : v;
+}
+
+/* Nearest e2m1 value of an exactly-held v, ties to the even code (mantissa bit
+ * 0), saturating at +-6; the sign of zero is kept.  A plain search over the
+ * eight magnitudes. */
+uint8_t orc_e2m1_from_f64(double v) {
+  uint8_t sign = signbit(v) ? 8 : 0;
+  double a = fabs(v);
+  if (!(a < 6.0)) return (uint8_t)(sign | 7);
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    double d = fabs(orc_e2m1_to_f64((uint8_t)c) - a);
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* The UE8M0 rule of orc_ue8m0_exponent for an element format whose largest
+ * magnitude is fmax: the smallest e in [-126, 127] with amax <= fmax * 2^e. */
+int32_t orc_mx_exponent(double amax, double fmax) {
+  int32_t e = -126;
+  while (e < 127 && amax > ldexp(fmax, e)) ++e;
+  return e;
+}
+
+/* MX weights: every 32 consecutive k of one row of w[G][N][K] share the
+ * exponent chosen directly from their largest magnitude, then each value is
+ * rounded to the element format.  fmt 0: e4m3 codes q[G][N][K]; fmt 1: e2m1
+ * codes two per byte, q[G][N][K/2], even k in the low nibble.  Scale bytes
+ * s[G][N][K/32] hold e + 127. */
+void orc_quant_weight_mx(const uint16_t* w, int32_t G, int32_t N, int32_t K, int32_t fmt,
+                         uint8_t* q, uint8_t* s) {
+  int32_t kb = K / 32;
+  double fmax = fmt == 0 ? 448.0 : 6.0;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int32_t g = 0; g < G; ++g)
+    for (int32_t n = 0; n < N; ++n) {
+      const uint16_t* row = w + ((int64_t)g * N + n) * K;
+      for (int32_t b = 0; b < kb; ++b) {
+        double amax = 0.0;
+        for (int32_t i = 0; i < 32; ++i) {
+          double a = fabs((double)orc_bf16_to_f32(row[b * 32 + i]));
+          if (a > amax) amax = a;
+        }
+        int32_t e = orc_mx_exponent(amax, fmax);
+        s[((int64_t)g * N + n) * kb + b] = (uint8_t)(e + 127);
+        for (int32_t i = 0; i < 32; ++i) {
+          int32_t kk = b * 32 + i;
+          double v = ldexp((double)orc_bf16_to_f32(row[kk]), -e);
+          if (fmt == 0) {
+            q[((int64_t)g * N + n) * K + kk] = orc_e4m3_from_f64(v);
+          } else {
+            uint8_t c = orc_e2m1_from_f64(v);
+            uint8_t* byte = q + ((int64_t)g * N + n) * (K / 2) + kk / 2;
+            *byte = (kk & 1) ? (uint8_t)((*byte & 0x0F) | (c << 4)) : (uint8_t)((*byte & 0xF0) | c);
+          }
+        }
+      }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* scatter                                                                   */
 /* ------------------------------------------------------------------------ */
 
@@ -426,6 +502,42 @@ void orc_gemm_fp8_rows(const uint8_t* A, const uint8_t* A_scale_rowmajor, int64_
     if (g < 0) continue;
     gemm_row_fp8(A + r * K, A_scale_rowmajor + r * kb, B + (int64_t)g * N * K,
                  B_scale + (int64_t)g * (N / 128) * kb, N, K, C + r * N);
+  }
+}
+
+/* FP8 activations (UE8M0 per 128 channels) times MX weights (one exponent per
+ * 32 k of a weight row): per 32-wide k block the products are summed in fp32
+ * (exact products), scaled by 2^(eA + eB) and the blocks accumulated in fp32
+ * in increasing order, as for the 128-block FP8 product. */
+void orc_gemm_mx_rows(const uint8_t* A, const uint8_t* A_scale_rowmajor, int64_t M,
+                      const uint8_t* B, const uint8_t* B_scale, int32_t fmt,
+                      int32_t N, int32_t K, const int32_t* row_group, uint16_t* C) {
+  int32_t ka = K / 128, kb = K / 32;
+  int64_t brow = fmt == 0 ? K : K / 2;
+  e4m3_table_init();
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < M; ++r) {
+    int32_t g = row_group[r];
+    if (g < 0) continue;
+    const uint8_t* a = A + r * K;
+    const uint8_t* as = A_scale_rowmajor + r * ka;
+    for (int32_t n = 0; n < N; ++n) {
+      const uint8_t* bn = B + ((int64_t)g * N + n) * brow;
+      const uint8_t* bs = B_scale + ((int64_t)g * N + n) * kb;
+      float acc = 0.0f;
+      for (int32_t blk = 0; blk < kb; ++blk) {
+        float part = 0.0f;
+        for (int32_t kk = blk * 32; kk < blk * 32 + 32; ++kk) {
+          float bv = fmt == 0 ? g_e4m3[bn[kk]]
+                              : (float)orc_e2m1_to_f64((uint8_t)((bn[kk / 2] >> (4 * (kk & 1))) & 15));
+          part += g_e4m3[a[kk]] * bv;
+        }
+        int32_t ea = (int32_t)as[blk / 4] - 127;
+        int32_t eb = (int32_t)bs[blk] - 127;
+        acc += (float)ldexp((double)part, ea + eb);
+      }
+      C[r * N + n] = orc_f64_to_bf16((double)acc);
+    }
   }
 }
 

@@ -57,6 +57,20 @@ void orc_quant_weight_blocks(const uint16_t* w, int32_t G, int32_t N, int32_t K,
 void orc_requant_weight_blocks(const uint8_t* q_in, const float* s_in, int32_t G, int32_t N,
                                int32_t K, uint8_t* q_out, uint8_t* s_out);
 
+/* MX weights (OCP microscaling: 32 consecutive k of a weight row share one
+ * E8M0 exponent, chosen with the UE8M0 rule; element format fmt 0 = e4m3,
+ * fmt 1 = e2m1 packed two per byte, even k in the low nibble).  Scales
+ * s[G][N][K/32]. */
+double   orc_e2m1_to_f64(uint8_t q);
+uint8_t  orc_e2m1_from_f64(double v);
+int32_t  orc_mx_exponent(double amax, double fmax);
+void orc_quant_weight_mx(const uint16_t* w, int32_t G, int32_t N, int32_t K, int32_t fmt,
+                         uint8_t* q, uint8_t* s);
+/* FP8 rows (UE8M0 per 128) times MX weights, blocks of 32 summed in fp32. */
+void orc_gemm_mx_rows(const uint8_t* A, const uint8_t* A_scale_rowmajor, int64_t M,
+                      const uint8_t* B, const uint8_t* B_scale, int32_t fmt,
+                      int32_t N, int32_t K, const int32_t* row_group, uint16_t* C);
+
 /* Compact layout (P1 implementation breakdown items 2-4). Returns 0, or 3 when
  * rows_capacity is below the rows the routing needs.  fp8 != 0 quantises each
  * scattered row (scale_out row-major [R][H/128]). */

@@ -25,6 +25,7 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 SIGNATURES = {
     "moe_compact_rows_bound": (_I64, [_I64, _I32, _I32]),
     "moe_use_masked_layout": (_I32, [_I32, _I32]),
+    "moe_choose_layout": (_I32, [_I64, _I32]),
     "moe_scatter_ws_bytes": (_SZ, [_I32, _I32, _I32]),
     "moe_status_str": (ctypes.c_char_p, [_I32]),
     "moe_get_device_error": (_I32, [_P, _P, _P]),
@@ -103,6 +104,13 @@ def moe_compact_rows_bound(num_assignments: int, num_local_experts: int, block_e
 
 def moe_use_masked_layout(num_experts: int, num_local_experts: int) -> bool:
     return bool(lib().moe_use_masked_layout(num_experts, num_local_experts))
+
+
+def moe_choose_layout(max_tokens: int, num_local_experts: int) -> bool:
+    r = lib().moe_choose_layout(max_tokens, num_local_experts)
+    if r < 0:
+        raise ValueError("moe_choose_layout: sizes must be positive")
+    return bool(r)
 
 
 def moe_scatter_ws_bytes(T: int, k: int, num_local_experts: int) -> int:

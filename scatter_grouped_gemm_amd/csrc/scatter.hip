@@ -284,6 +284,13 @@ extern "C" int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_
   return (num_experts > num_local_experts && num_local_experts <= 32) ? 1 : 0;
 }
 
+// Measured on MI355X: masked ahead up to ~1024 tokens, level from ~4096, where
+// its rows (one max_tokens slab per local expert) cost the most memory.
+extern "C" int32_t moe_choose_layout(int64_t max_tokens, int32_t num_local_experts) {
+  if (max_tokens <= 0 || num_local_experts <= 0) return -1;
+  return (max_tokens <= 2048 && max_tokens * num_local_experts <= (1ll << 20)) ? 1 : 0;
+}
+
 static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start, int32_t El,
                             int32_t block_e, const ScatterWs& w, int32_t* start_out,
                             int32_t* valid_out, bool masked, int32_t max_m, int32_t* src2dst,

@@ -39,6 +39,11 @@ def test_host_helpers_match_oracle(orc):
         assert L.moe_compact_rows_bound(A, E, B) == orc.compact_rows_bound(A, E, B)
     for E, El in [(256, 32), (256, 33), (8, 8), (64, 1), (32, 32)]:
         assert L.moe_use_masked_layout(E, El) == orc.use_masked_layout(E, El)
+    # the measured layout policy: masked up to 2048 tokens within 2^20 rows
+    for T, El, want in [(1, 256, 1), (2048, 256, 1), (2049, 8, 0), (4096, 32, 0), (2048, 513, 0),
+                        (1024, 1024, 1), (1024, 1025, 0)]:
+        assert L.moe_choose_layout(T, El) == bool(want), (T, El)
+    assert L.lib().moe_choose_layout(0, 8) == -1 and L.lib().moe_choose_layout(8, 0) == -1
     assert L.lib().moe_compact_rows_bound(-1, 8, 128) == -1
     assert L.lib().moe_compact_rows_bound(10, 0, 128) == -1
 

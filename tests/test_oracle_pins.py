@@ -606,3 +606,139 @@ def test_requant_dequantises_like_torch(orc):
     want = orc.quant_weight_blocks(inputs.bf16_bits(w_bf16))
     got = orc.requant_weight_blocks(q, s)
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+# ---------------------------------------------------------------------------
+# MX expert weights (the pages flag microscaled FP8 / FP4 weights as not yet
+# covered: "Support DeepGEMM for standard MoE dispatch", comments section)
+# ---------------------------------------------------------------------------
+
+def _e2m1_golden():
+    codes, vals = [], []
+    for line in open(os.path.join(GOLDEN, "ocp_mx_fp4_e2m1.txt")):
+        if line.strip() and not line.startswith("#"):
+            c, v = line.split()
+            codes.append(int(c, 16))
+            vals.append(float(v))
+    return np.array(codes), np.array(vals)
+
+
+def test_e2m1_decode_matches_spec_table(orc):
+    codes, vals = _e2m1_golden()
+    assert sorted(codes) == list(range(16))
+    for c, v in zip(codes, vals):
+        got = orc.e2m1_to_f64(int(c))
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), c
+
+
+def _e2m1_nearest_bruteforce(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code from the spec table, ties to the even code, saturating
+    at +-6; the sign of zero follows the input."""
+    codes, vals = _e2m1_golden()
+    pos = codes[(codes < 8)]
+    pv = vals[(codes < 8)]
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[:, None] - pv[None, :])
+    cand = d == d.min(axis=1, keepdims=True)
+    even = (pos[None, :] & 1) == 0
+    pick = np.where((cand & even).any(axis=1), np.argmax(cand & even, axis=1), np.argmax(cand, axis=1))
+    return (pos[pick] | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def test_e2m1_encoder_nearest_with_ties_to_even(orc):
+    grid = np.concatenate([np.arange(-130, 131) / 16.0, [-0.0, 7.0, -100.0, 0.2499, 0.2501],
+                           np.random.default_rng(3).normal(0, 3, 2000)])
+    ref = _e2m1_nearest_bruteforce(grid)
+    got = np.array([orc.e2m1_from_f64(float(v)) for v in grid], np.uint8)
+    assert np.array_equal(got, ref)
+    # the midpoints of the grid go to the even code
+    assert [orc.e2m1_from_f64(v) for v in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] == [0, 2, 2, 4, 4, 6, 6]
+
+
+def test_mx_exponent_closed_form(orc):
+    rng = np.random.default_rng(4)
+    for fmax in (448.0, 6.0):
+        for amax in np.concatenate([np.exp2(rng.uniform(-130, 130, 300)), [0.0]]):
+            e = orc.mx_exponent(float(amax), fmax)
+            want = -126 if amax == 0 else min(127, max(-126, math.ceil(math.log2(amax / fmax))))
+            assert e == want, (amax, fmax)
+        for e0 in (-20, 0, 5):                               # exact boundary and just past it
+            assert orc.mx_exponent(fmax * 2.0 ** e0, fmax) == e0
+            assert orc.mx_exponent(np.nextafter(fmax * 2.0 ** e0, np.inf), fmax) == e0 + 1
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_quant_weight_mx_rule(orc, fmt):
+    """Per 32 k of a row: exponent from the block maximum, codes = RNE of the
+    scaled values (torch's e4m3 cast, or the e2m1 table search), two e2m1
+    codes per byte with the even k in the low nibble."""
+    g = torch.Generator().manual_seed(6)
+    G, N, K = 2, 8, 96
+    w = torch.randn(G, N, K, generator=g) * torch.exp2(torch.randint(-12, 6, (G, N, K // 32, 1),
+                                                                      generator=g).float()).repeat_interleave(32, 2)[..., 0]
+    w[1, 3, 32:64] = 0
+    wb = w.to(torch.bfloat16)
+    q, s = orc.quant_weight_mx(inputs.bf16_bits(wb), fmt)
+    wf = wb.double().numpy()
+    fmax = 448.0 if fmt == "mxfp8" else 6.0
+    amax = np.abs(wf.reshape(G, N, K // 32, 32)).max(axis=3)
+    want_e = np.where(amax == 0, -126, np.clip(np.ceil(np.log2(np.maximum(amax, 1e-300) / fmax)), -126, 127))
+    assert np.array_equal(s.astype(np.int64) - 127, want_e.astype(np.int64))
+    scaled = wf * np.ldexp(1.0, -np.repeat(s.astype(np.int64) - 127, 32, axis=2))
+    if fmt == "mxfp8":
+        ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(q, ref)
+    else:
+        codes = _e2m1_nearest_bruteforce(scaled.reshape(-1)).reshape(G, N, K)
+        assert np.array_equal(q & 15, codes[:, :, 0::2]) and np.array_equal(q >> 4, codes[:, :, 1::2])
+
+
+def _mx_dequant(orc, q, s, fmt):
+    G, N, _ = q.shape
+    if fmt == "mxfp8":
+        vals = _e4m3_table()[q]
+    else:
+        _, tab = _e2m1_golden()
+        vals = np.empty((G, N, q.shape[2] * 2))
+        vals[:, :, 0::2] = tab[q & 15]
+        vals[:, :, 1::2] = tab[q >> 4]
+    return vals * np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=2)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_gemm_mx_against_numpy_dequantised(orc, fmt):
+    g = torch.Generator().manual_seed(7)
+    M, N, K, G = 20, 64, 256, 2
+    A = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    W = (torch.randn(G, N, K, generator=g) * 0.02).to(torch.bfloat16)
+    aq, as_ = orc.quant_rows(inputs.bf16_bits(A))
+    wq, ws = orc.quant_weight_mx(inputs.bf16_bits(W), fmt)
+    rg = (np.arange(M) % G).astype(np.int32)
+    rg[3] = -1
+    C = orc.gemm_mx_rows(aq, as_, wq, ws, fmt, rg)
+    Ad = _e4m3_table()[aq] * np.repeat(np.ldexp(1.0, as_.astype(np.int64) - 127), 128, axis=1)
+    Wd = _mx_dequant(orc, wq, ws, fmt)
+    ok = rg >= 0
+    ref = np.stack([Wd[rg[r]] @ Ad[r] for r in range(M) if ok[r]])
+    assert _rel_fro(_f32(C[ok]), ref) < 4e-3
+    assert np.all(C[~ok] == 0)
+    # integer codes, scales varied per 32-block and per 128-block: every partial
+    # sum is exact, so the result is the bf16 rounding of the exact product
+    qa = torch.randint(-4, 5, (M, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sa = np.full((M, K // 128), 127, np.uint8)
+    sa[:, 1] = 128
+    if fmt == "mxfp8":
+        qw = torch.randint(-4, 5, (G, N, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        lo = torch.randint(0, 16, (G, N, K // 2), generator=g).numpy()
+        hi = torch.randint(0, 16, (G, N, K // 2), generator=g).numpy()
+        qw = (lo | (hi << 4)).astype(np.uint8)
+    sw = np.full((G, N, K // 32), 127, np.uint8)
+    sw[1, 5, 3] = 125
+    sw[0, 7, 6] = 129
+    Ci = orc.gemm_mx_rows(qa, sa, qw, sw, fmt, rg)
+    Ad = _e4m3_table()[qa] * np.repeat(np.ldexp(1.0, sa.astype(np.int64) - 127), 128, axis=1)
+    Wd = _mx_dequant(orc, qw, sw, fmt)
+    for r in np.nonzero(ok)[0]:
+        exact = (Wd[rg[r]] @ Ad[r]).astype(np.float32)
+        assert np.array_equal(Ci[r], _bf16_of(exact))
