@@ -39,17 +39,20 @@ def parse():
                     help="target duration of the timed oracle run on the host")
     ap.add_argument("--unfused", action="store_true",
                     help="run w13 and SiLU-and-mul as two kernels")
+    ap.add_argument("--weight-format", default=None, choices=["block128", "mxfp8"],
+                    help="FP8 workloads: 128x128 UE8M0 weight blocks (default) or MX e4m3 weights")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
-def build_layer(wl, torch, fuse_silu=True):
+def build_layer(wl, torch, fuse_silu=True, weight_format=None):
     from scatter_grouped_gemm_amd import MoELayer, inputs
     layer = MoELayer(hidden=wl.H, intermediate=wl.I, num_experts=wl.E, top_k=wl.k, max_tokens=wl.T,
                      num_local_experts=wl.El, expert_start=wl.expert_start, fp8=wl.fp8,
                      layout=wl.layout, block_e=wl.block_e, max_m=wl.max_m or None,
-                     expected_m=wl.expected_m, fuse_silu=fuse_silu, device="cuda")
+                     expected_m=wl.expected_m, fuse_silu=fuse_silu, weight_format=weight_format,
+                     device="cuda")
     t0 = time.time()
     for e in range(wl.El):
         w13, w2 = inputs.expert_weights(wl, wl.expert_start + e, "cuda")
@@ -78,6 +81,8 @@ def gemm_work(wl, layer, torch):
     w13_flops = 2.0 * A * (2 * I) * H
     w2_flops = 2.0 * A * H * I
     sc = (1.0 / (128 * 128)) if wl.fp8 else 0.0          # weight block scales
+    if layer.weight_format == "mxfp8":
+        sc = 1.0 / 32                                      # one exponent per 32 k
     asc = (1.0 / 128) if wl.fp8 else 0.0                 # activation scales
     w13_out = (I * (ab + asc)) if layer.fuse_silu else (2 * I * 2)
     w13_bytes = active * 2 * I * H * (ab + sc) + A * H * (ab + asc) + A * w13_out
@@ -239,7 +244,8 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del a, b
-    layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused)
+    layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused,
+                                   weight_format=args.weight_format if wl.fp8 else None)
     for _ in range(args.warmup):
         layer(x, logits)
     torch.cuda.synchronize()
@@ -261,9 +267,10 @@ def main():
     roof = roofline(work["w13_flops"], work["w13_bytes"], kern[w13_key], dtype)
     roof["kernel"] = ("grouped_gemm w13 (gate/up) with SiLU-and-mul" if layer.fuse_silu
                       else "grouped_gemm w13 (gate/up)")
-    roof["traffic"] = measured_traffic(wl.name, "w13")
+    tkey = wl.name if layer.weight_format in ("block128", "bf16") else f"{wl.name}_{layer.weight_format}"
+    roof["traffic"] = measured_traffic(tkey, "w13")
     w2_roof = roofline(work["w2_flops"], work["w2_bytes"], kern["gemm_w2"], dtype)
-    w2_roof["traffic"] = measured_traffic(wl.name, "w2")
+    w2_roof["traffic"] = measured_traffic(tkey, "w2")
     gemm_ms = kern[w13_key] + kern["gemm_w2"]
     gemm_tflops = (work["w13_flops"] + work["w2_flops"]) / (gemm_ms * 1e-3) / 1e12
     res = {
@@ -282,7 +289,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
                    "E_local": wl.El, "top_k": wl.k, "layout": layer.layout, "block_e": wl.block_e,
                    "rows": layer.rows, "assignments": work["assignments"],
-                   "silu_fused_into_w13": layer.fuse_silu},
+                   "silu_fused_into_w13": layer.fuse_silu, "weight_format": layer.weight_format},
         "roofline": roof,
         "gemm": {"tflops_both": round(gemm_tflops, 1),
                  "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),
@@ -294,7 +301,7 @@ def main():
         res["requant_weights"] = requant_weights(wl, torch)
         log(f"requant of w13-shaped block-FP8 weights: {res['requant_weights']['ms']:.3f} ms, "
             f"{res['requant_weights']['achieved']:.0f} GB/s")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and layer.weight_format != "mxfp8":
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
     print(json.dumps(res), flush=True)
 

@@ -50,6 +50,10 @@ extern "C" {
 /* element types */
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_FP8_E4M3_UE8M0 1
+/* GEMM operand dtype: activations as MOE_DTYPE_FP8_E4M3_UE8M0, weights e4m3
+ * with MX scales (one UE8M0 exponent per 32 k of a weight row) in the tiled
+ * layout of moe_quant_weight_mx. */
+#define MOE_DTYPE_FP8_E4M3_MXFP8 2
 
 /* device error word bits (see moe_get_device_error) */
 #define MOE_DEVERR_MASKED_OVERFLOW 1  /* an expert received more than max_m rows */
@@ -189,6 +193,31 @@ int32_t moe_quant_fp8_ue8m0(const void* x, int64_t M, int32_t K, int64_t ld_x,
 int32_t moe_quant_weight_fp8_ue8m0(const void* w, int32_t G, int32_t N, int32_t K,
                                    uint8_t* q, uint8_t* scale, void* stream);
 
+/* MX expert weights (OCP microscaling: every 32 consecutive k of a weight row
+ * share one power-of-two scale), the weight format the pages flag as not yet
+ * covered ("Support DeepGEMM for standard MoE dispatch", comments section on
+ * FP4 and MX weights).  The exponent follows the pages' direct UE8M0 rule
+ * (implementation breakdown item 3) over each 32-value block: the smallest e in
+ * [-126, 127] with max|w| <= fmax * 2^e, fmax = 448 (e4m3) or 6 (e2m1); each
+ * value w * 2^-e is then rounded to nearest, ties to even.
+ *   w            device bf16 [G][N][K]
+ *   fmt          MOE_MX_E4M3: q e4m3 [G][N][K];
+ *                MOE_MX_E2M1: q e2m1 [G][N][K/2], two codes per byte, even k in
+ *                the low nibble (OCP FP4: sign, 2 exponent bits with bias 1,
+ *                1 mantissa bit)
+ *   scale_tiled  device u8 exponents + 127, tiled for the GEMM:
+ *                [G][N/64][K/128][4][16][4], the byte of (row n, 32-block b) at
+ *                ((g*(N/64) + n/64)*(K/128) + b/4)*256 + (b%4)*64 + (n%16)*4 + (n%64)/16
+ * Limits: N % 64 == 0, K % 128 == 0.  Non-finite weights: unspecified codes. */
+#define MOE_MX_E4M3 0
+#define MOE_MX_E2M1 1
+int32_t moe_quant_weight_mx(const void* w, int32_t G, int32_t N, int32_t K, int32_t fmt,
+                            uint8_t* q, uint8_t* scale_tiled, void* stream);
+/* Plain MX scales [G][N][K/32] (one byte per row and 32-block, as a checkpoint
+ * stores them) -> the tiled layout above. */
+int32_t moe_mx_scales_tile(const uint8_t* scale_plain, int32_t G, int32_t N, int32_t K,
+                           uint8_t* scale_tiled, void* stream);
+
 /* Requantise block-FP8 expert weights (a checkpoint's e4m3 codes with one
  * fp32 scale per 128x128 block) to the UE8M0 block format, through a bf16
  * intermediate ("Support DeepGEMM for standard MoE dispatch", implementation
@@ -208,9 +237,11 @@ int32_t moe_requant_weight_fp8_ue8m0(const uint8_t* q_in, const float* s_in, int
 
 /* Contiguous layout, P2 key source excerpts of _BF16GroupedContWarmupExecutor
  * and _run_bf16_contiguous_gemm: C[r, :] = A[r, :] . B[m_indices[r]]^T.
- *   dtype     MOE_DTYPE_BF16 (A bf16 [M][K], B bf16 [G][N][K]; scales NULL) or
+ *   dtype     MOE_DTYPE_BF16 (A bf16 [M][K], B bf16 [G][N][K]; scales NULL),
  *             MOE_DTYPE_FP8_E4M3_UE8M0 (A e4m3 [M][K] with A_scale [K/128][M],
- *             B e4m3 [G][N][K] with B_scale [G][N/128][K/128])
+ *             B e4m3 [G][N][K] with B_scale [G][N/128][K/128]) or
+ *             MOE_DTYPE_FP8_E4M3_MXFP8 (A as before, B e4m3 [G][N][K] with MX
+ *             B_scale tiled as moe_quant_weight_mx writes it)
  *   C         device bf16 [M][N].  Rows of an aligned 128-row block whose
  *             first row is -1 are not written; other rows with m_indices < 0
  *             (the padding at the end of an expert) receive unspecified values.

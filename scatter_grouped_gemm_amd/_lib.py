@@ -17,7 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 _lib = None
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EDEVICE = 0, 1, 2, 3, 4
-MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0 = 0, 1
+MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0, MOE_DTYPE_FP8_E4M3_MXFP8 = 0, 1, 2
+MOE_MX_E4M3, MOE_MX_E2M1 = 0, 1
 MOE_DEVERR_MASKED_OVERFLOW = 1
 
 # name -> (restype, argtypes); the exported symbols of include/moe.h
@@ -37,6 +38,8 @@ SIGNATURES = {
     "moe_quant_fp8_ue8m0": (_I32, [_P, _I64, _I32, _I64, _P, _P, _P, _P]),
     "moe_quant_weight_fp8_ue8m0": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_requant_weight_fp8_ue8m0": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_quant_weight_mx": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_mx_scales_tile": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
     "grouped_gemm_contig": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "grouped_gemm_masked": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "grouped_gemm_contig_silu": (_I32, [_I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32,
@@ -94,6 +97,16 @@ def _stream():
 
 def _dtype_code(fp8: bool) -> int:
     return MOE_DTYPE_FP8_E4M3_UE8M0 if fp8 else MOE_DTYPE_BF16
+
+
+def _gemm_dtype(fp8) -> int:
+    """GEMM operand dtype: False -> BF16, True -> FP8 with 128x128 weight
+    blocks, "mxfp8" -> FP8 activations with MX e4m3 weights."""
+    if fp8 == "mxfp8":
+        return MOE_DTYPE_FP8_E4M3_MXFP8
+    if isinstance(fp8, str):
+        raise ValueError(f"unknown GEMM weight format {fp8!r}")
+    return _dtype_code(bool(fp8))
 
 
 # --- host helpers ---------------------------------------------------------------
@@ -180,12 +193,33 @@ def moe_requant_weight_fp8_ue8m0(q_in, s_in, q_out, s_out):
         _ptr(q_in), _ptr(s_in), G, N, K, _ptr(q_out), _ptr(s_out), _stream()))
 
 
+def moe_quant_weight_mx(w, fmt, q, scale_tiled):
+    """bf16 w [G,N,K] -> MX codes q (e4m3 [G,N,K] or e2m1 pairs [G,N,K/2]) and
+    tiled scales scale_tiled [G, N/64, K/128, 256]."""
+    G, N, K = w.shape
+    f = {"e4m3": MOE_MX_E4M3, "e2m1": MOE_MX_E2M1}[fmt]
+    assert w.dtype == torch.bfloat16 and q.dtype == torch.uint8 and scale_tiled.dtype == torch.uint8
+    assert q.shape == (G, N, K if f == MOE_MX_E4M3 else K // 2)
+    assert scale_tiled.numel() == G * N * (K // 32)
+    _check("moe_quant_weight_mx", lib().moe_quant_weight_mx(
+        _ptr(w), G, N, K, f, _ptr(q), _ptr(scale_tiled), _stream()))
+
+
+def moe_mx_scales_tile(scale_plain, scale_tiled):
+    """Plain MX scales [G,N,K/32] -> the GEMM's tiled layout."""
+    G, N, KB = scale_plain.shape
+    assert scale_plain.dtype == torch.uint8 and scale_tiled.dtype == torch.uint8
+    assert scale_tiled.numel() == scale_plain.numel()
+    _check("moe_mx_scales_tile", lib().moe_mx_scales_tile(
+        _ptr(scale_plain), G, N, KB * 32, _ptr(scale_tiled), _stream()))
+
+
 def grouped_gemm_contig(fp8, A, A_scale, B, B_scale, C, m_indices):
     M, K = A.shape
     G, N, K2 = B.shape
     assert K == K2 and C.shape == (M, N) and C.dtype == torch.bfloat16
     _check("grouped_gemm_contig", lib().grouped_gemm_contig(
-        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(m_indices),
+        _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(m_indices),
         M, N, K, G, _stream()))
 
 
@@ -194,7 +228,7 @@ def grouped_gemm_masked(fp8, A, A_scale, B, B_scale, C, masked_m, expected_m):
     G2, N, K2 = B.shape
     assert G == G2 and K == K2 and C.shape == (G, max_m, N) and C.dtype == torch.bfloat16
     _check("grouped_gemm_masked", lib().grouped_gemm_masked(
-        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(masked_m),
+        _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(masked_m),
         expected_m, max_m, N, K, G, _stream()))
 
 
@@ -207,7 +241,7 @@ def grouped_gemm_contig_silu(fp8, A, A_scale, B, B_scale, out, m_indices, out_sc
     q8 = out.dtype == torch.uint8
     assert K == K2 and out.shape == (M, I) and (q8 or out.dtype == torch.bfloat16)
     _check("grouped_gemm_contig_silu", lib().grouped_gemm_contig_silu(
-        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
+        _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
         _ptr(out), _ptr(out_scale), _ptr(m_indices), M, I, K, G, _stream()))
 
 
@@ -221,7 +255,7 @@ def grouped_gemm_masked_silu(fp8, A, A_scale, B, B_scale, out, masked_m, expecte
     q8 = out.dtype == torch.uint8
     assert G == G2 and K == K2 and out.shape == (G, max_m, I) and (q8 or out.dtype == torch.bfloat16)
     _check("grouped_gemm_masked_silu", lib().grouped_gemm_masked_silu(
-        _dtype_code(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
+        _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _dtype_code(q8),
         _ptr(out), _ptr(out_scale), _ptr(masked_m), expected_m, max_m, I, K, G, _stream()))
 
 

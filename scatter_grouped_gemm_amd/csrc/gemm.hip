@@ -88,17 +88,23 @@ constexpr int kMaxMaskedGroups = 1024;
 constexpr int kPrefixLen = kMaxMaskedGroups + 17;
 static_assert(kPrefixLen * 4 <= kRunMax * 8, "the prefix array lives in the run-table space");
 
+// Weight formats (template argument WF): 0 bf16; 1 e4m3 with one UE8M0
+// exponent per 128x128 block; 2 e4m3 MX (one exponent per 32 k of a weight
+// row, scales in the tiled layout below).
+constexpr int kWfBf16 = 0, kWfFp8Block = 1, kWfMxFp8 = 2;
 // Stage: the data rows, then for FP8 the scale slots of the BM/64 wavefronts
-// fetching activation scales and one shared by the rest (weight scales).
-template <int BM, int BN, bool FP8>
+// fetching activation scales and the weight scales: one slot shared by the
+// rest (128x128 blocks), or for MX one 256-byte slot per 64 tile columns.
+template <int BM, int BN, int WF>
 constexpr int gemm_stage_bytes() {
-  return (BM + BN) * 128 + (FP8 ? (BM / 64 + 1) * kScaleSlot : 0);
+  return (BM + BN) * 128 +
+         (WF == kWfBf16 ? 0 : (BM / 64 + (WF == kWfMxFp8 ? BN / 64 : 1)) * kScaleSlot);
 }
 // LDS: stages, the run table and, for the FP8 SiLU epilogue, the per-row
 // maxima of the column wavefronts.
-template <int BM, int BN, bool FP8, int EPI>
+template <int BM, int BN, int WF, int EPI>
 constexpr int gemm_lds_bytes() {
-  return kStages * gemm_stage_bytes<BM, BN, FP8>() + kRunMax * 8 +
+  return kStages * gemm_stage_bytes<BM, BN, WF>() + kRunMax * 8 +
          (EPI == kEpiSiluFp8 ? BM * (kWaves / (BM >= 128 ? 2 : 1)) * 4 : 0);
 }
 
@@ -235,16 +241,18 @@ __device__ __forceinline__ void tile_rows(const GemmArgs& p, const TilePos& t, i
   }
 }
 
-template <int BM, int BN, bool FP8, bool MASKED, int EPI>
+template <int BM, int BN, int WF, bool MASKED, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  constexpr bool FP8 = WF != kWfBf16;
+  constexpr bool MX = WF == kWfMxFp8;
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
   constexpr int WAVES_N = kWaves / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ROWS = BM + BN;
   constexpr int SDATA = ROWS * 128;                      // stage data bytes
-  constexpr int STAGE = gemm_stage_bytes<BM, BN, FP8>();
+  constexpr int STAGE = gemm_stage_bytes<BM, BN, WF>();
   constexpr int NLD = ROWS / (8 * kWaves);  // 16-byte direct loads per wavefront per stage
   constexpr int NVM = NLD + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step
   constexpr int NB = BN / 128;              // weight-scale blocks per tile
@@ -424,6 +432,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // the weight-scale array between the tile's two 128-column blocks
   constexpr int NBW = EPI == kEpiPlain ? BN : 128;
   const int64_t bs_stride = EPI == kEpiPlain ? KB : static_cast<int64_t>(p.N / 256) * KB;
+  // MX weight scales: wavefront w >= ASW fetches the 256-byte slot of tile
+  // column block c_w (64 columns; SiLU tiles: gate blocks 0-1, up blocks 2-3)
+  constexpr int NMX = BN / 64;
+  const int c_w = wave >= ASW ? (wave - ASW) % NMX : 0;
   int d_rows;
   uint32_t soff[NLD];  // per-lane source offsets from the tile's A / B rows
   // A direct load moves 8 rows (64 lanes x 16 bytes) into LDS; lane i carries
@@ -437,7 +449,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     d_pos = (pos_);                                                                           \
     d_aoff = r0_ * rowbytes;                                                                  \
     d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * NBW) * rowbytes; \
-    d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * (NBW / 128)) * KB;            \
+    if constexpr (MX) {                                                                       \
+      const int blk_ = EPI == kEpiPlain ? t_.nt * NMX + c_w                                   \
+                                        : (c_w >= 2 ? p.N / 128 : 0) + t_.nt * 2 + (c_w & 1); \
+      d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 64) + blk_) * KB * 256;                   \
+    } else {                                                                                  \
+      d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * (NBW / 128)) * KB;          \
+    }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                         \
       const int R_ = (wave * NLD + j) * 8 + (lane >> 3);                                      \
       const int c_ = (lane & 7) ^ lds_swz(R_);                                                \
@@ -466,10 +484,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
         const int nb_ = lane < NB ? lane : NB - 1;                                              \
         src_ = p.B_scale + d_bs0 + nb_ * bs_stride + d_k;                                       \
       }                                                                                         \
-      /* wavefronts past ASW all write the same bytes into one slot */                          \
-      __builtin_amdgcn_global_load_lds(src_,                                                    \
-          (__attribute__((address_space(3))) void*)(stg_ + SDATA + (wave < ASW ? wave : ASW) * kScaleSlot), \
-          1, 0, 0);                                                                             \
+      if (!MX || wave < ASW) {                                                                  \
+        /* wavefronts past ASW all write the same bytes into one slot */                        \
+        __builtin_amdgcn_global_load_lds(src_,                                                  \
+            (__attribute__((address_space(3))) void*)(stg_ + SDATA + (wave < ASW ? wave : ASW) * kScaleSlot), \
+            1, 0, 0);                                                                           \
+      } else {                                                                                  \
+        /* MX: the slot of block c_w for this k-step, 4 bytes per lane; waves */                \
+        /* past ASW + NMX repeat a slot with the same bytes */                                  \
+        __builtin_amdgcn_global_load_lds(p.B_scale + d_bs0 + static_cast<int64_t>(d_k) * 256 + lane * 4, \
+            (__attribute__((address_space(3))) void*)(stg_ + SDATA + (ASW + c_w) * kScaleSlot), \
+            4, 0, 0);                                                                           \
+      }                                                                                         \
     }                                                                                           \
     const uint8_t* ab_ = p.A + d_aoff + static_cast<int64_t>(d_k) * 128;                        \
     const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * 128;                        \
@@ -514,6 +540,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int frag_row = lane & 15;
   const int frag_k = lane >> 4;
   const int wblk = (wn * WN) / 128;
+  // MX: the wavefront's first weight-scale slot and byte: its columns start at
+  // tile column wn*WN (SiLU tiles: gate column wn*CH, up slot two further on);
+  // scale byte j16 of a slot dword serves the 16 columns 16*j16 .. of that block
+  const int mx_c0 = (EPI == kEpiPlain ? wn * WN : wn * CH) / 64;
+  const int mx_j0 = ((EPI == kEpiPlain ? wn * WN : wn * CH) % 64) / 16;
   // Fragment rows are (multiple of 16) + frag_row, so the chunk permutation
   // depends on the lane only: the byte offset of logical chunk c of the lane's
   // row in the sub-tile starting at stage row rb is rb*128 + frag_row*128 +
@@ -521,6 +552,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int swz_l = lds_swz(frag_row);
 #define MOE_ROWOFF(rb_, c_) ((rb_) * 128 + frag_row * 128 + (((c_) ^ swz_l) << 4))
 
+  // FP8 operands of the 16x16x128 MFMA: the hardware reads bytes 0-15 of lane
+  // group g's 32 as k = 16g .. 16g+15 and bytes 16-31 as k = 64+16g .. (its
+  // 32-wide scale blocks are k = 32b .. 32b+31, scale of row i, block b from
+  // lane 16b + i), so each lane takes 16-byte chunks g and g + 4 of the
+  // 128-byte k-step: the instruction's k order is then the memory order and an
+  // MX scale byte per lane covers one contiguous 32-block.
   using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
   constexpr int KS = FP8 ? 1 : 2;  // MFMA k-substeps per 128-byte stage
   struct Frags {
@@ -536,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                        \
         const int rb_ = wm * WM + im * 16;                                                       \
         if constexpr (FP8) {                                                                     \
-          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2));     \
-          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2 + 1)); \
+          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k));         \
+          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k + 4));     \
           F_.a[ks][im] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
                                  (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
         } else {                                                                                 \
@@ -547,8 +584,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                        \
         const int rb_ = BM + wn * WN + jn * 16;                                                  \
         if constexpr (FP8) {                                                                     \
-          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2));     \
-          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k * 2 + 1)); \
+          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k));         \
+          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k + 4));     \
           F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
                                  (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
         } else {                                                                                 \
@@ -560,8 +597,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       const uint8_t* X_ = S_ + SDATA;                                                            \
       _Pragma("unroll") for (int im = 0; im < TM; ++im)                                          \
         F_.sa[im] = X_[(wm * WM + im * 16 + frag_row) * 4];                                      \
-      F_.sw = X_[ASW * kScaleSlot + (EPI == kEpiPlain ? wblk : 0) * 4];                          \
-      F_.sw2 = X_[ASW * kScaleSlot + 4];                                                         \
+      if constexpr (MX) {                                                                        \
+        const uint8_t* M_ = X_ + ASW * kScaleSlot + frag_k * 64 + frag_row * 4;                 \
+        F_.sw = *reinterpret_cast<const int*>(M_ + mx_c0 * kScaleSlot);                          \
+        if (EPI != kEpiPlain) F_.sw2 = *reinterpret_cast<const int*>(M_ + (mx_c0 + 2) * kScaleSlot); \
+      } else {                                                                                   \
+        F_.sw = X_[ASW * kScaleSlot + (EPI == kEpiPlain ? wblk : 0) * 4];                        \
+        F_.sw2 = X_[ASW * kScaleSlot + 4];                                                       \
+      }                                                                                          \
     }                                                                                            \
   } while (0)
 #define MOE_MMA(F_)                                                                              \
@@ -572,7 +615,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
           if constexpr (FP8)                                                                     \
             acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                      \
                 F_.b[ks][jn], F_.a[ks][im], acc[jn][im], 0, 0, 0,                                \
-                (EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw, 0, F_.sa[im]);              \
+                MX ? (((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw) >>                   \
+                      (8 * (mx_j0 + (EPI != kEpiPlain ? jn % (TN / 2) : jn))))                    \
+                   : ((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw),                      \
+                0, F_.sa[im]);                                                                   \
           else                                                                                   \
             acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F_.b[ks][jn], F_.a[ks][im],    \
                                                                   acc[jn][im], 0, 0, 0);         \
@@ -773,7 +819,7 @@ static int persistent_grid() {
   return grid[dev];
 }
 
-template <int BM, int BN, bool FP8, bool MASKED, int EPI = kEpiPlain>
+template <int BM, int BN, int WF, bool MASKED, int EPI = kEpiPlain>
 int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   // The compact run table holds one XCD's share of the M-tiles (about a
   // million rows in all) and tile positions are 32-bit.
@@ -786,9 +832,9 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   const int64_t tiles = order_m * a.n_tiles;
   if (tiles == 0) return MOE_OK;
   if (tiles >= (1ll << 31)) return MOE_EUNSUPPORTED;
-  constexpr int lds = gemm_lds_bytes<BM, BN, FP8, EPI>();
+  constexpr int lds = gemm_lds_bytes<BM, BN, WF, EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = grouped_gemm_kernel<BM, BN, FP8, MASKED, EPI>;
+  auto kern = grouped_gemm_kernel<BM, BN, WF, MASKED, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -803,6 +849,17 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   return MOE_OK;
 }
 
+// Weight format of a GEMM dtype -> the kernel instance.
+template <int BM, int BN, bool MASKED, int EPI = kEpiPlain>
+int32_t launch_dtype(int32_t dtype, const GemmArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case MOE_DTYPE_BF16: return launch_gemm<BM, BN, kWfBf16, MASKED, EPI>(a, s);
+    case MOE_DTYPE_FP8_E4M3_UE8M0: return launch_gemm<BM, BN, kWfFp8Block, MASKED, EPI>(a, s);
+    case MOE_DTYPE_FP8_E4M3_MXFP8: return launch_gemm<BM, BN, kWfMxFp8, MASKED, EPI>(a, s);
+    default: return MOE_EUNSUPPORTED;
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -810,9 +867,11 @@ using namespace moe;
 static int32_t validate_gemm(int32_t dtype, const void* A, const uint8_t* A_scale, const void* B,
                              const uint8_t* B_scale, void* C, int32_t N, int32_t K, int32_t G) {
   if (N <= 0 || K <= 0 || G <= 0) return MOE_EINVAL;
-  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0 &&
+      dtype != MOE_DTYPE_FP8_E4M3_MXFP8)
+    return MOE_EUNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
-  if (dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
+  if (dtype != MOE_DTYPE_BF16 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
   if (K > (1 << 22)) return MOE_EUNSUPPORTED;  // per-lane 32-bit source offsets
   if (!A || !B || !C) return MOE_EINVAL;
   return MOE_OK;
@@ -839,10 +898,8 @@ extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
-  if (N % 256 == 0)
-    return fp8 ? launch_gemm<128, 256, true, false>(a, s) : launch_gemm<128, 256, false, false>(a, s);
-  return fp8 ? launch_gemm<128, 128, true, false>(a, s) : launch_gemm<128, 128, false, false>(a, s);
+  if (N % 256 == 0) return launch_dtype<128, 256, false>(dtype, a, s);
+  return launch_dtype<128, 128, false>(dtype, a, s);
 }
 
 extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
@@ -866,15 +923,14 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   const bool n256 = N % 256 == 0;
   // tile height from the hint: small expected counts waste less work on 64 rows
   if (expected_m > 0 && expected_m <= 64) {
-    if (n256) return fp8 ? launch_gemm<64, 256, true, true>(a, s) : launch_gemm<64, 256, false, true>(a, s);
-    return fp8 ? launch_gemm<64, 128, true, true>(a, s) : launch_gemm<64, 128, false, true>(a, s);
+    if (n256) return launch_dtype<64, 256, true>(dtype, a, s);
+    return launch_dtype<64, 128, true>(dtype, a, s);
   }
-  if (n256) return fp8 ? launch_gemm<128, 256, true, true>(a, s) : launch_gemm<128, 256, false, true>(a, s);
-  return fp8 ? launch_gemm<128, 128, true, true>(a, s) : launch_gemm<128, 128, false, true>(a, s);
+  if (n256) return launch_dtype<128, 256, true>(dtype, a, s);
+  return launch_dtype<128, 128, true>(dtype, a, s);
 }
 
 // The w13 GEMM with SiLU-and-mul in its epilogue: B holds [G][2I][K] (gate
@@ -912,12 +968,9 @@ extern "C" int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const 
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
-    return fp8 ? launch_gemm<128, 256, true, false, kEpiSiluFp8>(a, s)
-               : launch_gemm<128, 256, false, false, kEpiSiluFp8>(a, s);
-  return fp8 ? launch_gemm<128, 256, true, false, kEpiSiluBf16>(a, s)
-             : launch_gemm<128, 256, false, false, kEpiSiluBf16>(a, s);
+    return launch_dtype<128, 256, false, kEpiSiluFp8>(dtype, a, s);
+  return launch_dtype<128, 256, false, kEpiSiluBf16>(dtype, a, s);
 }
 
 extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
@@ -946,16 +999,11 @@ extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const 
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   const bool q8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
   if (expected_m > 0 && expected_m <= 64) {
-    if (q8) return fp8 ? launch_gemm<64, 256, true, true, kEpiSiluFp8>(a, s)
-                       : launch_gemm<64, 256, false, true, kEpiSiluFp8>(a, s);
-    return fp8 ? launch_gemm<64, 256, true, true, kEpiSiluBf16>(a, s)
-               : launch_gemm<64, 256, false, true, kEpiSiluBf16>(a, s);
+    if (q8) return launch_dtype<64, 256, true, kEpiSiluFp8>(dtype, a, s);
+    return launch_dtype<64, 256, true, kEpiSiluBf16>(dtype, a, s);
   }
-  if (q8) return fp8 ? launch_gemm<128, 256, true, true, kEpiSiluFp8>(a, s)
-                     : launch_gemm<128, 256, false, true, kEpiSiluFp8>(a, s);
-  return fp8 ? launch_gemm<128, 256, true, true, kEpiSiluBf16>(a, s)
-             : launch_gemm<128, 256, false, true, kEpiSiluBf16>(a, s);
+  if (q8) return launch_dtype<128, 256, true, kEpiSiluFp8>(dtype, a, s);
+  return launch_dtype<128, 256, true, kEpiSiluBf16>(dtype, a, s);
 }

@@ -197,6 +197,94 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
   }
 }
 
+// MX weights: byte offset of the scale of (row n of group g, 32-block b) in
+// the tiled layout [G][N/64][K/128][4][16][4]: per 64 weight rows and 128 k, a
+// 256-byte slot whose byte kq*64 + r16*4 + j16 holds row 16*j16 + r16 of the
+// slot and k block 4*s + kq -- so a lane of the GEMM reads the four scales of
+// its 16-row sub-tiles with one 4-byte LDS load.
+__device__ __forceinline__ int64_t mx_scale_offset(int64_t g, int n, int b, int N, int K) {
+  const int c = n & 63;
+  return ((g * (N / 64) + n / 64) * (K / 128) + b / 4) * 256 + (b & 3) * 64 + (c & 15) * 4 +
+         (c >> 4);
+}
+
+// UE8M0 rule for e2m1 elements (largest magnitude 6 = 1.5 * 2^2): the
+// smallest e in [-126, 127] with amax <= 6 * 2^e.
+__device__ __forceinline__ int mx_exponent_e2m1(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = static_cast<int>(u >> 23);
+  if (ef == 0) return -126;
+  const int e = ef - 127 - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+// e2m1 code of v (nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even
+// code, saturating at 6, sign kept): the midpoints between neighbours decide.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return sign | c;
+}
+
+// One thread per 32 consecutive k of a weight row: exponent from the block
+// maximum, then e4m3 (fmt 0, 32 bytes) or e2m1 (fmt 1, 16 bytes, even k in
+// the low nibble) codes.
+__global__ __launch_bounds__(256) void quant_weight_mx_kernel(const uint16_t* __restrict__ w,
+                                                              int64_t rows, int N, int K, int fmt,
+                                                              uint8_t* __restrict__ q,
+                                                              uint8_t* __restrict__ s_tiled) {
+  const int kb = K / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * kb) return;
+  const int64_t row = i / kb;
+  const int b = static_cast<int>(i - row * kb);
+  const uint16_t* src = w + row * K + b * 32;
+  float f[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float t[8];
+    unpack8(*reinterpret_cast<const uint4*>(src + 8 * j), t);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f[8 * j + u] = t[u];
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  const int64_t so = mx_scale_offset(row / N, static_cast<int>(row % N), b, N, K);
+  if (fmt == MOE_MX_E4M3) {
+    const int e = ue8m0_exponent(amax);
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = e4m3x4(f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3], e);
+    uint4* dst = reinterpret_cast<uint4*>(q + row * K + b * 32);
+    dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+    dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    s_tiled[so] = static_cast<uint8_t>(e + 127);
+  } else {
+    const int e = mx_exponent_e2m1(amax);
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      c[j / 8] |= f32_to_e2m1(__builtin_amdgcn_ldexpf(f[j], -e)) << (4 * (j % 8));
+    *reinterpret_cast<uint4*>(q + row * (K / 2) + b * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+    s_tiled[so] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+// Plain MX scales [G][N][K/32] -> the tiled layout, one thread per byte.
+__global__ __launch_bounds__(256) void mx_scales_tile_kernel(const uint8_t* __restrict__ s_plain,
+                                                             int64_t total, int N, int K,
+                                                             uint8_t* __restrict__ s_tiled) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int kb = K / 32;
+  const int64_t row = i / kb;
+  const int b = static_cast<int>(i - row * kb);
+  s_tiled[mx_scale_offset(row / N, static_cast<int>(row % N), b, N, K)] = s_plain[i];
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -212,6 +300,38 @@ extern "C" int32_t moe_quant_fp8_ue8m0(const void* x, int64_t M, int32_t K, int6
   if (nb >= (1ll << 31)) return MOE_EINVAL;
   quant_rows_kernel<<<static_cast<int>(nb), 256, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint16_t*>(x), M, K, ld_x, m_indices, q, scale);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_quant_weight_mx(const void* w, int32_t G, int32_t N, int32_t K,
+                                       int32_t fmt, uint8_t* q, uint8_t* scale_tiled,
+                                       void* stream) {
+  if (G < 0 || N <= 0 || K <= 0) return MOE_EINVAL;
+  if (fmt != MOE_MX_E4M3 && fmt != MOE_MX_E2M1) return MOE_EUNSUPPORTED;
+  if (N % 64 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (G == 0) return MOE_OK;
+  if (!w || !q || !scale_tiled) return MOE_EINVAL;
+  const int64_t threads = static_cast<int64_t>(G) * N * (K / 32);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks >= (1ll << 31)) return MOE_EINVAL;
+  quant_weight_mx_kernel<<<static_cast<int>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(w), static_cast<int64_t>(G) * N, N, K, fmt, q, scale_tiled);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_mx_scales_tile(const uint8_t* scale_plain, int32_t G, int32_t N, int32_t K,
+                                      uint8_t* scale_tiled, void* stream) {
+  if (G < 0 || N <= 0 || K <= 0) return MOE_EINVAL;
+  if (N % 64 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
+  if (G == 0) return MOE_OK;
+  if (!scale_plain || !scale_tiled) return MOE_EINVAL;
+  const int64_t total = static_cast<int64_t>(G) * N * (K / 32);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks >= (1ll << 31)) return MOE_EINVAL;
+  mx_scales_tile_kernel<<<static_cast<int>(blocks), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      scale_plain, total, N, K, scale_tiled);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -27,11 +27,20 @@ class MoELayer:
                  max_tokens: int, num_local_experts: int | None = None, expert_start: int = 0,
                  fp8: bool = False, layout: str = "auto", block_e: int = 128,
                  max_m: int | None = None, expected_m: int = 0, fuse_silu: bool = True,
-                 device="cuda"):
+                 weight_format: str | None = None, device="cuda"):
         self.H, self.I, self.E, self.k = hidden, intermediate, num_experts, top_k
         self.El = num_local_experts or num_experts
         self.expert_start = expert_start
         self.fp8 = fp8
+        # FP8 weights: 128x128 UE8M0 blocks (default) or "mxfp8" (one exponent
+        # per 32 k of a weight row); activations are FP8 with 128-channel scales
+        # either way
+        if weight_format not in (None, "block128", "mxfp8"):
+            raise ValueError(f"unknown weight format {weight_format!r}")
+        if weight_format == "mxfp8" and not fp8:
+            raise ValueError("MX weights need the FP8 activation path")
+        self.weight_format = weight_format or ("block128" if fp8 else "bf16")
+        self.wdt = "mxfp8" if self.weight_format == "mxfp8" else fp8
         self.block_e = block_e
         self.T_max = max_tokens
         self.device = torch.device(device)
@@ -91,7 +100,10 @@ class MoELayer:
         wdt = torch.uint8 if self.fp8 else torch.bfloat16
         self.w13 = torch.empty(El, 2 * I, H, dtype=wdt, device=d)
         self.w2 = torch.empty(El, H, I, dtype=wdt, device=d)
-        if self.fp8:
+        if self.weight_format == "mxfp8":
+            self.w13_scale = torch.empty(El, 2 * I // 64, H // 128, 256, dtype=torch.uint8, device=d)
+            self.w2_scale = torch.empty(El, H // 64, I // 128, 256, dtype=torch.uint8, device=d)
+        elif self.fp8:
             self.w13_scale = torch.empty(El, 2 * I // 128, H // 128, dtype=torch.uint8, device=d)
             self.w2_scale = torch.empty(El, H // 128, I // 128, dtype=torch.uint8, device=d)
 
@@ -103,6 +115,10 @@ class MoELayer:
         if not self.fp8:
             self.w13[e].copy_(w13)
             self.w2[e].copy_(w2)
+            return
+        if self.weight_format == "mxfp8":
+            L.moe_quant_weight_mx(w13.contiguous()[None], "e4m3", self.w13[e:e + 1], self.w13_scale[e:e + 1])
+            L.moe_quant_weight_mx(w2.contiguous()[None], "e4m3", self.w2[e:e + 1], self.w2_scale[e:e + 1])
             return
         L.moe_quant_weight_fp8_ue8m0(w13.contiguous()[None], self.w13[e:e + 1], self.w13_scale[e:e + 1])
         L.moe_quant_weight_fp8_ue8m0(w2.contiguous()[None], self.w2[e:e + 1], self.w2_scale[e:e + 1])
@@ -118,6 +134,8 @@ class MoELayer:
         through bf16."""
         if not self.fp8:
             raise ValueError("block-FP8 weights given to a BF16 layer: the activation dtype follows the weights")
+        if self.weight_format != "block128":
+            raise ValueError("block-FP8 checkpoint weights requantise to 128x128 UE8M0 blocks")
         if self.w13 is None:
             self.allocate_weights()
         L.moe_requant_weight_fp8_ue8m0(w13q.contiguous(), w13s.contiguous(), self.w13, self.w13_scale)
@@ -147,7 +165,7 @@ class MoELayer:
         else:
             ids, tw = topk_ids, topk_weights
         s2d = self.src2dst[:T]
-        fp8 = self.fp8
+        fp8, wdt = self.fp8, self.wdt
         I = self.I
         if self.layout == "compact":
             with self._mark("scatter"):
@@ -156,16 +174,16 @@ class MoELayer:
                                       self.expert_start_loc, self.num_valid, s2d, self.ws)
             if self.fuse_silu:
                 with self._mark("gemm_w13_silu"):
-                    L.grouped_gemm_contig_silu(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
+                    L.grouped_gemm_contig_silu(wdt, self.x_buf, self.x_scale, self.w13, self.w13_scale,
                                                self.act, self.m_indices, self.act_scale)
             else:
                 with self._mark("gemm_w13"):
-                    L.grouped_gemm_contig(fp8, self.x_buf, self.x_scale, self.w13, self.w13_scale,
+                    L.grouped_gemm_contig(wdt, self.x_buf, self.x_scale, self.w13, self.w13_scale,
                                           self.gateup, self.m_indices)
                 with self._mark("silu_and_mul"):
                     L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, m_indices=self.m_indices)
             with self._mark("gemm_w2"):
-                L.grouped_gemm_contig(fp8, self.act, self.act_scale, self.w2, self.w2_scale, self.y,
+                L.grouped_gemm_contig(wdt, self.act, self.act_scale, self.w2, self.w2_scale, self.y,
                                       self.m_indices)
         else:
             El, mm = self.El, self.max_m
@@ -174,19 +192,19 @@ class MoELayer:
                                      self.x_scale, self.masked_m, s2d, self.ws)
             if self.fuse_silu:
                 with self._mark("gemm_w13_silu"):
-                    L.grouped_gemm_masked_silu(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
+                    L.grouped_gemm_masked_silu(wdt, self.x_buf.view(El, mm, self.H), self.x_scale,
                                                self.w13, self.w13_scale, self.act.view(El, mm, I),
                                                self.masked_m, self.expected_m, self.act_scale)
             else:
                 with self._mark("gemm_w13"):
-                    L.grouped_gemm_masked(fp8, self.x_buf.view(El, mm, self.H), self.x_scale,
+                    L.grouped_gemm_masked(wdt, self.x_buf.view(El, mm, self.H), self.x_scale,
                                           self.w13, self.w13_scale, self.gateup.view(El, mm, 2 * I),
                                           self.masked_m, self.expected_m)
                 with self._mark("silu_and_mul"):
                     L.silu_and_mul(self.gateup, self.act, fp8, self.act_scale, masked_m=self.masked_m,
                                    max_m=mm)
             with self._mark("gemm_w2"):
-                L.grouped_gemm_masked(fp8, self.act.view(El, mm, I), self.act_scale, self.w2,
+                L.grouped_gemm_masked(wdt, self.act.view(El, mm, I), self.act_scale, self.w2,
                                       self.w2_scale, self.y.view(El, mm, self.H), self.masked_m,
                                       self.expected_m)
         out = self.out[:T]

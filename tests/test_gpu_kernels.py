@@ -261,6 +261,125 @@ def test_requant_then_gemm_matches_dequantised_weights(orc):
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
 
 
+def _mx_tile(s_plain: np.ndarray) -> np.ndarray:
+    """Plain MX scales [G,N,K/32] in the GEMM's tiled order
+    [G][N/64][K/128][kq][r16][j16] (row 64*b + 16*j16 + r16, k block 4*s + kq)."""
+    G, N, KB = s_plain.shape
+    t = s_plain.reshape(G, N // 64, 4, 16, KB // 4, 4)          # g, b, j16, r16, s, kq
+    return np.ascontiguousarray(t.transpose(0, 1, 4, 5, 3, 2)).reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_quant_weight_mx(orc, fmt):
+    announce("quant_weight_mx", fmt)
+    g = torch.Generator().manual_seed(8)
+    G, N, K = 3, 192, 384
+    w = torch.randn(G, N, K, generator=g) * torch.exp2(
+        torch.randint(-10, 8, (G, N, K // 32), generator=g).float()).repeat_interleave(32, 2)
+    w[1, 5, 64:96] = 0
+    w[2, 70, :32] = 6.0 * 2.0 ** -3                  # exactly the e2m1 maximum at a power of two
+    w = w.to(torch.bfloat16)
+    q_ref, s_ref = orc.quant_weight_mx(bits(w), fmt)
+    q = poison(q_ref.shape, torch.uint8)
+    st = poison((G * N * K // 32,), torch.uint8)
+    L.moe_quant_weight_mx(w.to(DEV), "e4m3" if fmt == "mxfp8" else "e2m1", q, st)
+    st2 = poison((G * N * K // 32,), torch.uint8)
+    L.moe_mx_scales_tile(torch.from_numpy(s_ref).to(DEV), st2)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(st.cpu().numpy(), _mx_tile(s_ref))
+    assert np.array_equal(st2.cpu().numpy(), _mx_tile(s_ref))
+
+
+def _mx_operands(orc, M_counts, N, K, seed, integer_valued=False):
+    """FP8 activations (128-channel scales) and MXFP8 weights."""
+    G = len(M_counts)
+    m_idx = compact_layout(M_counts)
+    M = len(m_idx)
+    g = torch.Generator().manual_seed(seed)
+    if integer_valued:
+        qa = torch.randint(-4, 5, (M, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        qb = torch.randint(-4, 5, (G, N, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        rng = np.random.default_rng(seed)
+        # exponents within +-1 keep every partial sum exact in fp32
+        sa = rng.integers(126, 129, (M, K // 128)).astype(np.uint8)
+        sb = rng.integers(126, 129, (G, N, K // 32)).astype(np.uint8)
+    else:
+        A = torch.randn(M, K, generator=g).to(torch.bfloat16)
+        B = (torch.randn(G, N, K, generator=g) * 0.02).to(torch.bfloat16)
+        qa, sa = orc.quant_rows(bits(A))
+        qb, sb = orc.quant_weight_mx(bits(B), "mxfp8")
+    return dict(m_idx=m_idx, A=qa, As=sa, B=qb, Bs=sb)
+
+
+@pytest.mark.parametrize("integer_valued", [False, True])
+@pytest.mark.parametrize("counts,N,K", [([130, 0, 5, 256, 1, 300], 256, 384), ([64, 129], 384, 512)])
+def test_gemm_mxfp8_contig(orc, counts, N, K, integer_valued):
+    """FP8 activations times MX e4m3 weights (one exponent per 32 k): the
+    per-lane scale of the block-scaled MFMA; exact on integer-valued codes."""
+    announce("gemm_mxfp8_contig", counts, N, K, integer_valued)
+    ops = _mx_operands(orc, counts, N, K, seed=N + K, integer_valued=integer_valued)
+    ref = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], "mxfp8", ops["m_idx"])
+    M = len(ops["m_idx"])
+    C = poison((M, N), torch.bfloat16)
+    L.grouped_gemm_contig("mxfp8", u8_dev(ops["A"]), u8_dev(ops["As"].T.copy()), u8_dev(ops["B"]),
+                          u8_dev(_mx_tile(ops["Bs"])), C, i32_dev(ops["m_idx"]))
+    torch.cuda.synchronize()
+    got = bits(C)
+    valid = ops["m_idx"] >= 0
+    if integer_valued:
+        assert np.array_equal(got[valid], ref[valid])
+    else:
+        _check_close(got, ref, valid, 2e-2, True)
+
+
+@pytest.mark.parametrize("expected_m", [0, 8])
+def test_gemm_mxfp8_masked(orc, expected_m):
+    announce("gemm_mxfp8_masked", expected_m)
+    G, max_m, N, K = 5, 200, 256, 384
+    masked = np.array([0, 1, 200, 37, 130], np.int32)
+    ops = _mx_operands(orc, [max_m] * G, N, K, seed=31, integer_valued=True)
+    rg = orc.masked_row_group(masked, max_m)
+    A = ops["A"][: G * max_m]
+    As = ops["As"][: G * max_m]
+    ref = orc.gemm_mx_rows(A, As, ops["B"], ops["Bs"], "mxfp8", rg)
+    C = poison((G, max_m, N), torch.bfloat16)
+    As_dev = As.reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
+    L.grouped_gemm_masked("mxfp8", u8_dev(A).view(G, max_m, K), u8_dev(As_dev), u8_dev(ops["B"]),
+                          u8_dev(_mx_tile(ops["Bs"])), C, i32_dev(masked), expected_m)
+    torch.cuda.synchronize()
+    got = bits(C).reshape(G * max_m, N)
+    valid = rg >= 0
+    assert np.array_equal(got[valid], ref[valid])
+
+
+@pytest.mark.parametrize("out_fp8", [False, True])
+def test_gemm_mxfp8_silu_fused_matches_separate(orc, out_fp8):
+    """MX weights through the fused w13 + SiLU-and-mul epilogue (gate and up
+    scale slots) equal the plain MX GEMM followed by silu_and_mul, bit for bit."""
+    announce("gemm_mxfp8_silu", out_fp8)
+    I, K = 256, 384
+    ops = _mx_operands(orc, [130, 0, 5, 256, 1, 300], 2 * I, K, seed=41)
+    M = len(ops["m_idx"])
+    m_dev = i32_dev(ops["m_idx"])
+    A, As, B, Bs = u8_dev(ops["A"]), u8_dev(ops["As"].T.copy()), u8_dev(ops["B"]), u8_dev(_mx_tile(ops["Bs"]))
+    gu = poison((M, 2 * I), torch.bfloat16)
+    L.grouped_gemm_contig("mxfp8", A, As, B, Bs, gu, m_dev)
+    odt = torch.uint8 if out_fp8 else torch.bfloat16
+    sep, fus = poison((M, I), odt), poison((M, I), odt)
+    ss = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    fs = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    L.silu_and_mul(gu, sep, out_fp8, ss, m_indices=m_dev)
+    L.grouped_gemm_contig_silu("mxfp8", A, As, B, Bs, fus, m_dev, fs)
+    torch.cuda.synchronize()
+    valid = ops["m_idx"] >= 0
+    assert np.array_equal(fus.view(torch.uint8).cpu().numpy()[valid], sep.view(torch.uint8).cpu().numpy()[valid])
+    if out_fp8:
+        assert np.array_equal(fs.cpu().numpy()[:, valid], ss.cpu().numpy()[:, valid])
+    h1 = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], "mxfp8", ops["m_idx"])
+    _check_close(bits(gu), h1, valid, 2e-2, True)
+
+
 # ---------------------------------------------------------------------------
 # grouped GEMMs
 # ---------------------------------------------------------------------------
