@@ -39,7 +39,7 @@ def parse():
                     help="target duration of the timed oracle run on the host")
     ap.add_argument("--unfused", action="store_true",
                     help="run w13 and SiLU-and-mul as two kernels")
-    ap.add_argument("--weight-format", default=None, choices=["block128", "mxfp8"],
+    ap.add_argument("--weight-format", default=None, choices=["block128", "mxfp8", "mxfp4"],
                     help="FP8 workloads: 128x128 UE8M0 weight blocks (default) or MX e4m3 weights")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -81,12 +81,14 @@ def gemm_work(wl, layer, torch):
     w13_flops = 2.0 * A * (2 * I) * H
     w2_flops = 2.0 * A * H * I
     sc = (1.0 / (128 * 128)) if wl.fp8 else 0.0          # weight block scales
-    if layer.weight_format == "mxfp8":
+    wb = ab
+    if layer.mx:
         sc = 1.0 / 32                                      # one exponent per 32 k
+        wb = 0.5 if layer.weight_format == "mxfp4" else 1.0
     asc = (1.0 / 128) if wl.fp8 else 0.0                 # activation scales
     w13_out = (I * (ab + asc)) if layer.fuse_silu else (2 * I * 2)
-    w13_bytes = active * 2 * I * H * (ab + sc) + A * H * (ab + asc) + A * w13_out
-    w2_bytes = active * H * I * (ab + sc) + A * I * (ab + asc) + A * H * 2
+    w13_bytes = active * 2 * I * H * (wb + sc) + A * H * (ab + asc) + A * w13_out
+    w2_bytes = active * H * I * (wb + sc) + A * I * (ab + asc) + A * H * 2
     return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
                 w13_bytes=w13_bytes, w2_bytes=w2_bytes)
 
@@ -301,7 +303,7 @@ def main():
         res["requant_weights"] = requant_weights(wl, torch)
         log(f"requant of w13-shaped block-FP8 weights: {res['requant_weights']['ms']:.3f} ms, "
             f"{res['requant_weights']['achieved']:.0f} GB/s")
-    if not args.no_cpu_baseline and layer.weight_format != "mxfp8":
+    if not args.no_cpu_baseline and not layer.mx:
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
     print(json.dumps(res), flush=True)
 

@@ -54,6 +54,10 @@ extern "C" {
  * with MX scales (one UE8M0 exponent per 32 k of a weight row) in the tiled
  * layout of moe_quant_weight_mx. */
 #define MOE_DTYPE_FP8_E4M3_MXFP8 2
+/* GEMM operand dtype: activations as MOE_DTYPE_FP8_E4M3_UE8M0, weights e2m1
+ * [G][N][K/2] (moe_quant_weight_mx with MOE_MX_E2M1) with the same tiled MX
+ * scales. */
+#define MOE_DTYPE_FP8_MXFP4 3
 
 /* device error word bits (see moe_get_device_error) */
 #define MOE_DEVERR_MASKED_OVERFLOW 1  /* an expert received more than max_m rows */
@@ -241,7 +245,8 @@ int32_t moe_requant_weight_fp8_ue8m0(const uint8_t* q_in, const float* s_in, int
  *             MOE_DTYPE_FP8_E4M3_UE8M0 (A e4m3 [M][K] with A_scale [K/128][M],
  *             B e4m3 [G][N][K] with B_scale [G][N/128][K/128]) or
  *             MOE_DTYPE_FP8_E4M3_MXFP8 (A as before, B e4m3 [G][N][K] with MX
- *             B_scale tiled as moe_quant_weight_mx writes it)
+ *             B_scale tiled as moe_quant_weight_mx writes it) or
+ *             MOE_DTYPE_FP8_MXFP4 (A as before, B e2m1 [G][N][K/2], MX scales)
  *   C         device bf16 [M][N].  Rows of an aligned 128-row block whose
  *             first row is -1 are not written; other rows with m_indices < 0
  *             (the padding at the end of an expert) receive unspecified values.
@@ -285,7 +290,8 @@ int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale
  *   Rows follow the underlying GEMM: rows of blocks whose first row is -1
  *   (compact) or at or past masked_m rounded up to 128 (masked) are not
  *   written; other rows past an expert's valid rows receive unspecified values.
- * Limits: I % 128 == 0, I <= 2^29; the rest as the underlying GEMM. */
+ * Limits: I % 128 == 0, (I + 256) * K * 2 < 2^32; the rest as the underlying
+ * GEMM. */
 int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const uint8_t* A_scale,
                                  const void* B, const uint8_t* B_scale, int32_t out_dtype,
                                  void* out, uint8_t* out_scale, const int32_t* m_indices,

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 _lib = None
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EDEVICE = 0, 1, 2, 3, 4
-MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0, MOE_DTYPE_FP8_E4M3_MXFP8 = 0, 1, 2
+MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0, MOE_DTYPE_FP8_E4M3_MXFP8, MOE_DTYPE_FP8_MXFP4 = 0, 1, 2, 3
 MOE_MX_E4M3, MOE_MX_E2M1 = 0, 1
 MOE_DEVERR_MASKED_OVERFLOW = 1
 
@@ -104,6 +104,8 @@ def _gemm_dtype(fp8) -> int:
     blocks, "mxfp8" -> FP8 activations with MX e4m3 weights."""
     if fp8 == "mxfp8":
         return MOE_DTYPE_FP8_E4M3_MXFP8
+    if fp8 == "mxfp4":
+        return MOE_DTYPE_FP8_MXFP4
     if isinstance(fp8, str):
         raise ValueError(f"unknown GEMM weight format {fp8!r}")
     return _dtype_code(bool(fp8))
@@ -214,9 +216,15 @@ def moe_mx_scales_tile(scale_plain, scale_tiled):
         _ptr(scale_plain), G, N, KB * 32, _ptr(scale_tiled), _stream()))
 
 
+def _bk(fp8, B):
+    """(G, N, K) of a weight tensor: e2m1 weights hold two k per byte."""
+    G, N, Kb = B.shape
+    return G, N, Kb * 2 if fp8 == "mxfp4" else Kb
+
+
 def grouped_gemm_contig(fp8, A, A_scale, B, B_scale, C, m_indices):
     M, K = A.shape
-    G, N, K2 = B.shape
+    G, N, K2 = _bk(fp8, B)
     assert K == K2 and C.shape == (M, N) and C.dtype == torch.bfloat16
     _check("grouped_gemm_contig", lib().grouped_gemm_contig(
         _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(m_indices),
@@ -225,7 +233,7 @@ def grouped_gemm_contig(fp8, A, A_scale, B, B_scale, C, m_indices):
 
 def grouped_gemm_masked(fp8, A, A_scale, B, B_scale, C, masked_m, expected_m):
     G, max_m, K = A.shape
-    G2, N, K2 = B.shape
+    G2, N, K2 = _bk(fp8, B)
     assert G == G2 and K == K2 and C.shape == (G, max_m, N) and C.dtype == torch.bfloat16
     _check("grouped_gemm_masked", lib().grouped_gemm_masked(
         _gemm_dtype(fp8), _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(masked_m),
@@ -236,7 +244,7 @@ def grouped_gemm_contig_silu(fp8, A, A_scale, B, B_scale, out, m_indices, out_sc
     """w13 GEMM with SiLU-and-mul fused: out [M][I] is bf16, or e4m3 (uint8)
     with out_scale [I/128][M]."""
     M, K = A.shape
-    G, N, K2 = B.shape
+    G, N, K2 = _bk(fp8, B)
     I = N // 2
     q8 = out.dtype == torch.uint8
     assert K == K2 and out.shape == (M, I) and (q8 or out.dtype == torch.bfloat16)
@@ -250,7 +258,7 @@ def grouped_gemm_masked_silu(fp8, A, A_scale, B, B_scale, out, masked_m, expecte
     """Masked-layout w13 GEMM with SiLU-and-mul fused: out [G][max_m][I];
     FP8 out_scale [G][I/128][max_m]."""
     G, max_m, K = A.shape
-    G2, N, K2 = B.shape
+    G2, N, K2 = _bk(fp8, B)
     I = N // 2
     q8 = out.dtype == torch.uint8
     assert G == G2 and K == K2 and out.shape == (G, max_m, I) and (q8 or out.dtype == torch.bfloat16)

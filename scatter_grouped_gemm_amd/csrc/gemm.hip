@@ -90,15 +90,18 @@ static_assert(kPrefixLen * 4 <= kRunMax * 8, "the prefix array lives in the run-
 
 // Weight formats (template argument WF): 0 bf16; 1 e4m3 with one UE8M0
 // exponent per 128x128 block; 2 e4m3 MX (one exponent per 32 k of a weight
-// row, scales in the tiled layout below).
-constexpr int kWfBf16 = 0, kWfFp8Block = 1, kWfMxFp8 = 2;
+// row, scales in the tiled layout of the MX quantiser); 3 e2m1 MX (two codes
+// per byte, even k in the low nibble, same scales).
+constexpr int kWfBf16 = 0, kWfFp8Block = 1, kWfMxFp8 = 2, kWfMxFp4 = 3;
+// bytes of one weight row in one 128-byte activation k-step
+constexpr int weight_row_bytes(int wf) { return wf == kWfMxFp4 ? 64 : 128; }
 // Stage: the data rows, then for FP8 the scale slots of the BM/64 wavefronts
 // fetching activation scales and the weight scales: one slot shared by the
 // rest (128x128 blocks), or for MX one 256-byte slot per 64 tile columns.
 template <int BM, int BN, int WF>
 constexpr int gemm_stage_bytes() {
-  return (BM + BN) * 128 +
-         (WF == kWfBf16 ? 0 : (BM / 64 + (WF == kWfMxFp8 ? BN / 64 : 1)) * kScaleSlot);
+  return BM * 128 + BN * weight_row_bytes(WF) +
+         (WF == kWfBf16 ? 0 : (BM / 64 + (WF >= kWfMxFp8 ? BN / 64 : 1)) * kScaleSlot);
 }
 // LDS: stages, the run table and, for the FP8 SiLU epilogue, the per-row
 // maxima of the column wavefronts.
@@ -245,21 +248,22 @@ template <int BM, int BN, int WF, bool MASKED, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr bool FP8 = WF != kWfBf16;
-  constexpr bool MX = WF == kWfMxFp8;
+  constexpr bool MX = WF >= kWfMxFp8;
+  constexpr bool W4 = WF == kWfMxFp4;
+  constexpr int BROW = weight_row_bytes(WF);             // stage bytes of a weight row
   constexpr int WAVES_M = BM >= 128 ? 2 : 1;
   constexpr int WAVES_N = kWaves / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int ROWS = BM + BN;
-  constexpr int SDATA = ROWS * 128;                      // stage data bytes
+  constexpr int SDATA = BM * 128 + BN * BROW;            // stage data bytes
   constexpr int STAGE = gemm_stage_bytes<BM, BN, WF>();
-  constexpr int NLD = ROWS / (8 * kWaves);  // 16-byte direct loads per wavefront per stage
+  constexpr int NLD = SDATA / (1024 * kWaves);  // 16-byte direct loads per wavefront per stage
   constexpr int NVM = NLD + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step
   constexpr int NB = BN / 128;              // weight-scale blocks per tile
   constexpr int ASW = BM / 64;              // wavefronts fetching activation scales
   static_assert(BM % 64 == 0 && BN % 128 == 0 && WN <= 128 && WM % 16 == 0 && WN % 16 == 0,
                 "tile shape");
-  static_assert(ROWS % (8 * kWaves) == 0, "stage rows split evenly over the wavefronts");
+  static_assert(SDATA % (1024 * kWaves) == 0, "stage bytes split evenly over the wavefronts");
   static_assert(ASW < kWaves, "a wavefront is left for the weight scales");
   // The SiLU epilogue takes gate block nt and up block nt into one tile, laid
   // out in the stage as chunks of CH = WN/2 rows gate, up, gate, up, ... so
@@ -417,7 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 
   // ======== the flat k-step stream ========
   constexpr int ES = FP8 ? 1 : 2;
-  const int64_t rowbytes = static_cast<int64_t>(p.K) * ES;
+  const int64_t rowbytes = static_cast<int64_t>(p.K) * ES;  // activation row
+  const int64_t browbytes = rowbytes / 128 * BROW;          // weight row
   const int nk = static_cast<int>(rowbytes / 128);
   const int KB = p.K / 128;
   const int G = p.G;
@@ -438,9 +443,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int c_w = wave >= ASW ? (wave - ASW) % NMX : 0;
   int d_rows;
   uint32_t soff[NLD];  // per-lane source offsets from the tile's A / B rows
-  // A direct load moves 8 rows (64 lanes x 16 bytes) into LDS; lane i carries
-  // the 16-byte chunk that belongs at LDS position i of its row, i.e. source
-  // chunk (i & 7) ^ swz(row).  Stage rows [0, BM) are A rows, [BM, ROWS) B rows.
+  // A direct load moves 1 KB (64 lanes x 16 bytes) into LDS: 8 activation rows,
+  // or 1024 / BROW weight rows; lane i carries the 16-byte chunk that belongs
+  // at LDS position i, i.e. source chunk (i & 7) ^ swz(row) of a 128-byte row,
+  // or (i & 3) ^ ((row >> 2) & 3) of a 64-byte e2m1 row.  The stage holds the
+  // BM activation rows, then the BN weight rows.
 #define MOE_DSET(pos_)                                                                        \
   do {                                                                                        \
     const TilePos t_ = map_pos<MASKED>(table, i_lo, n_tiles, used, (pos_));                         \
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     tile_rows<BM, MASKED>(p, t_, r0_, d_rows, d_as0);                                         \
     d_pos = (pos_);                                                                           \
     d_aoff = r0_ * rowbytes;                                                                  \
-    d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * NBW) * rowbytes; \
+    d_boff = (static_cast<int64_t>(t_.g) * p.N + static_cast<int64_t>(t_.nt) * NBW) * browbytes; \
     if constexpr (MX) {                                                                       \
       const int blk_ = EPI == kEpiPlain ? t_.nt * NMX + c_w                                   \
                                         : (c_w >= 2 ? p.N / 128 : 0) + t_.nt * 2 + (c_w & 1); \
@@ -457,12 +464,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * (NBW / 128)) * KB;          \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                         \
-      const int R_ = (wave * NLD + j) * 8 + (lane >> 3);                                      \
-      const int c_ = (lane & 7) ^ lds_swz(R_);                                                \
-      int r_ = R_ < BM ? (R_ < d_rows ? R_ : d_rows - 1) : R_ - BM;                           \
-      if (EPI != kEpiPlain && R_ >= BM)                                                       \
-        r_ = ((r_ / CH) & 1) * (p.N / 2) + (r_ / (2 * CH)) * CH + (r_ % CH);                  \
-      soff[j] = static_cast<uint32_t>(r_ * rowbytes + c_ * 16);                               \
+      const int q_ = wave * NLD + j;                                                          \
+      if (q_ * 1024 < BM * 128) {                                                             \
+        const int R_ = q_ * 8 + (lane >> 3);                                                  \
+        const int c_ = (lane & 7) ^ lds_swz(R_);                                              \
+        const int r_ = R_ < d_rows ? R_ : d_rows - 1;                                         \
+        soff[j] = static_cast<uint32_t>(r_ * rowbytes + c_ * 16);                             \
+      } else {                                                                                \
+        const int b_ = (q_ * 1024 - BM * 128) / BROW + lane / (BROW / 16);                    \
+        const int c_ = W4 ? (lane & 3) ^ ((b_ >> 2) & 3) : (lane & 7) ^ lds_swz(b_);          \
+        int r_ = b_;                                                                          \
+        if (EPI != kEpiPlain)                                                                 \
+          r_ = ((r_ / CH) & 1) * (p.N / 2) + (r_ / (2 * CH)) * CH + (r_ % CH);                \
+        soff[j] = static_cast<uint32_t>(r_ * browbytes + c_ * 16);                            \
+      }                                                                                       \
     }                                                                                         \
   } while (0)
   MOE_DSET(d_pos);
@@ -498,10 +513,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       }                                                                                         \
     }                                                                                           \
     const uint8_t* ab_ = p.A + d_aoff + static_cast<int64_t>(d_k) * 128;                        \
-    const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * 128;                        \
+    const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * BROW;                       \
     uint8_t* const dst_ = stg_ + wave * NLD * 1024;                                             \
     _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                           \
-      const bool is_a_ = (wave * NLD + j) * 8 < BM;                                             \
+      const bool is_a_ = (wave * NLD + j) * 1024 < BM * 128;                                    \
       __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                           \
           (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);                \
     }                                                                                           \
@@ -550,6 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // row in the sub-tile starting at stage row rb is rb*128 + frag_row*128 +
   // ((c ^ swz_l) << 4).
   const int swz_l = lds_swz(frag_row);
+  const int swz4_l = (frag_row >> 2) & 3;  // e2m1 weight rows: 64 bytes, 4 chunks
 #define MOE_ROWOFF(rb_, c_) ((rb_) * 128 + frag_row * 128 + (((c_) ^ swz_l) << 4))
 
   // FP8 operands of the 16x16x128 MFMA: the hardware reads bytes 0-15 of lane
@@ -583,7 +599,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       }                                                                                          \
       _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                        \
         const int rb_ = BM + wn * WN + jn * 16;                                                  \
-        if constexpr (FP8) {                                                                     \
+        if constexpr (W4) {                                                                      \
+          /* e2m1: lane group g holds k 32g .. 32g+31, 16 bytes of the 64-byte row */           \
+          const u32x4_t v_ = *reinterpret_cast<const u32x4_t*>(                                  \
+              S_ + BM * 128 + (wn * WN + jn * 16 + frag_row) * 64 + ((frag_k ^ swz4_l) << 4));   \
+          F_.b[ks][jn] = i32x8_t{(int)v_[0], (int)v_[1], (int)v_[2], (int)v_[3], 0, 0, 0, 0};    \
+        } else if constexpr (FP8) {                                                              \
           const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k));         \
           const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, frag_k + 4));     \
           F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
@@ -614,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
         _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
           if constexpr (FP8)                                                                     \
             acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                      \
-                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], 0, 0, 0,                                \
+                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], W4 ? 4 : 0, 0, 0,                       \
                 MX ? (((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw) >>                   \
                       (8 * (mx_j0 + (EPI != kEpiPlain ? jn % (TN / 2) : jn))))                    \
                    : ((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw),                      \
@@ -856,6 +877,7 @@ int32_t launch_dtype(int32_t dtype, const GemmArgs& a, hipStream_t s) {
     case MOE_DTYPE_BF16: return launch_gemm<BM, BN, kWfBf16, MASKED, EPI>(a, s);
     case MOE_DTYPE_FP8_E4M3_UE8M0: return launch_gemm<BM, BN, kWfFp8Block, MASKED, EPI>(a, s);
     case MOE_DTYPE_FP8_E4M3_MXFP8: return launch_gemm<BM, BN, kWfMxFp8, MASKED, EPI>(a, s);
+    case MOE_DTYPE_FP8_MXFP4: return launch_gemm<BM, BN, kWfMxFp4, MASKED, EPI>(a, s);
     default: return MOE_EUNSUPPORTED;
   }
 }
@@ -868,7 +890,7 @@ static int32_t validate_gemm(int32_t dtype, const void* A, const uint8_t* A_scal
                              const uint8_t* B_scale, void* C, int32_t N, int32_t K, int32_t G) {
   if (N <= 0 || K <= 0 || G <= 0) return MOE_EINVAL;
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_UE8M0 &&
-      dtype != MOE_DTYPE_FP8_E4M3_MXFP8)
+      dtype != MOE_DTYPE_FP8_E4M3_MXFP8 && dtype != MOE_DTYPE_FP8_MXFP4)
     return MOE_EUNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0) return MOE_EUNSUPPORTED;
   if (dtype != MOE_DTYPE_BF16 && (!A_scale || !B_scale)) return MOE_EUNSUPPORTED;
@@ -951,6 +973,8 @@ extern "C" int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const 
   int32_t st = validate_silu(out_dtype, out, out_scale, I);
   if (st != MOE_OK) return st;
   if (I > (1 << 29)) return MOE_EUNSUPPORTED;
+  // per-lane 32-bit offsets reach the up rows, I weight rows in
+  if (static_cast<int64_t>(I + 256) * K * 2 >= (1ll << 32)) return MOE_EUNSUPPORTED;
   st = validate_gemm(dtype, A, A_scale, B, B_scale, out, 2 * I, K, G);
   if (st != MOE_OK) return st;
   if (M == 0) return MOE_OK;
@@ -982,6 +1006,7 @@ extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const 
   int32_t st = validate_silu(out_dtype, out, out_scale, I);
   if (st != MOE_OK) return st;
   if (I > (1 << 29)) return MOE_EUNSUPPORTED;
+  if (static_cast<int64_t>(I + 256) * K * 2 >= (1ll << 32)) return MOE_EUNSUPPORTED;
   st = validate_gemm(dtype, A, A_scale, B, B_scale, out, 2 * I, K, G);
   if (st != MOE_OK) return st;
   if (!masked_m) return MOE_EINVAL;

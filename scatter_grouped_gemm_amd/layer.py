@@ -35,12 +35,13 @@ class MoELayer:
         # FP8 weights: 128x128 UE8M0 blocks (default) or "mxfp8" (one exponent
         # per 32 k of a weight row); activations are FP8 with 128-channel scales
         # either way
-        if weight_format not in (None, "block128", "mxfp8"):
+        if weight_format not in (None, "block128", "mxfp8", "mxfp4"):
             raise ValueError(f"unknown weight format {weight_format!r}")
-        if weight_format == "mxfp8" and not fp8:
+        if weight_format in ("mxfp8", "mxfp4") and not fp8:
             raise ValueError("MX weights need the FP8 activation path")
         self.weight_format = weight_format or ("block128" if fp8 else "bf16")
-        self.wdt = "mxfp8" if self.weight_format == "mxfp8" else fp8
+        self.mx = self.weight_format in ("mxfp8", "mxfp4")
+        self.wdt = self.weight_format if self.mx else fp8
         self.block_e = block_e
         self.T_max = max_tokens
         self.device = torch.device(device)
@@ -98,9 +99,10 @@ class MoELayer:
     def allocate_weights(self):
         d, El, H, I = self.device, self.El, self.H, self.I
         wdt = torch.uint8 if self.fp8 else torch.bfloat16
-        self.w13 = torch.empty(El, 2 * I, H, dtype=wdt, device=d)
-        self.w2 = torch.empty(El, H, I, dtype=wdt, device=d)
-        if self.weight_format == "mxfp8":
+        half = 2 if self.weight_format == "mxfp4" else 1      # e2m1: two k per byte
+        self.w13 = torch.empty(El, 2 * I, H // half, dtype=wdt, device=d)
+        self.w2 = torch.empty(El, H, I // half, dtype=wdt, device=d)
+        if self.mx:
             self.w13_scale = torch.empty(El, 2 * I // 64, H // 128, 256, dtype=torch.uint8, device=d)
             self.w2_scale = torch.empty(El, H // 64, I // 128, 256, dtype=torch.uint8, device=d)
         elif self.fp8:
@@ -116,9 +118,10 @@ class MoELayer:
             self.w13[e].copy_(w13)
             self.w2[e].copy_(w2)
             return
-        if self.weight_format == "mxfp8":
-            L.moe_quant_weight_mx(w13.contiguous()[None], "e4m3", self.w13[e:e + 1], self.w13_scale[e:e + 1])
-            L.moe_quant_weight_mx(w2.contiguous()[None], "e4m3", self.w2[e:e + 1], self.w2_scale[e:e + 1])
+        if self.mx:
+            f = "e4m3" if self.weight_format == "mxfp8" else "e2m1"
+            L.moe_quant_weight_mx(w13.contiguous()[None], f, self.w13[e:e + 1], self.w13_scale[e:e + 1])
+            L.moe_quant_weight_mx(w2.contiguous()[None], f, self.w2[e:e + 1], self.w2_scale[e:e + 1])
             return
         L.moe_quant_weight_fp8_ue8m0(w13.contiguous()[None], self.w13[e:e + 1], self.w13_scale[e:e + 1])
         L.moe_quant_weight_fp8_ue8m0(w2.contiguous()[None], self.w2[e:e + 1], self.w2_scale[e:e + 1])

@@ -96,7 +96,8 @@ def test_validation_rejects_before_launch():
     assert lib.moe_mx_scales_tile(P, 2, 128, 100, P, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_mx_scales_tile(None, 2, 128, 128, P, None) == L.MOE_EINVAL
     assert lib.grouped_gemm_contig(2, P, None, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
-    assert lib.grouped_gemm_contig(3, P, P, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(4, P, P, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_contig(3, P, None, P, P, P, P, 256, 256, 256, 2, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_requant_weight_fp8_ue8m0(P, P, -1, 128, 128, P, P, None) == L.MOE_EINVAL
     assert lib.moe_requant_weight_fp8_ue8m0(P, None, 2, 128, 128, P, P, None) == L.MOE_EINVAL
     assert lib.moe_requant_weight_fp8_ue8m0(None, None, 0, 128, 128, None, None, None) == L.MOE_OK

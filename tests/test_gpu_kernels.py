@@ -291,15 +291,18 @@ def test_quant_weight_mx(orc, fmt):
     assert np.array_equal(st2.cpu().numpy(), _mx_tile(s_ref))
 
 
-def _mx_operands(orc, M_counts, N, K, seed, integer_valued=False):
-    """FP8 activations (128-channel scales) and MXFP8 weights."""
+def _mx_operands(orc, M_counts, N, K, seed, integer_valued=False, fmt="mxfp8"):
+    """FP8 activations (128-channel scales) and MX weights (e4m3 or e2m1)."""
     G = len(M_counts)
     m_idx = compact_layout(M_counts)
     M = len(m_idx)
     g = torch.Generator().manual_seed(seed)
     if integer_valued:
         qa = torch.randint(-4, 5, (M, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        qb = torch.randint(-4, 5, (G, N, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        if fmt == "mxfp8":
+            qb = torch.randint(-4, 5, (G, N, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        else:                                                       # every e2m1 code pair
+            qb = torch.randint(0, 256, (G, N, K // 2), generator=g).to(torch.uint8).numpy()
         rng = np.random.default_rng(seed)
         # exponents within +-1 keep every partial sum exact in fp32
         sa = rng.integers(126, 129, (M, K // 128)).astype(np.uint8)
@@ -308,21 +311,23 @@ def _mx_operands(orc, M_counts, N, K, seed, integer_valued=False):
         A = torch.randn(M, K, generator=g).to(torch.bfloat16)
         B = (torch.randn(G, N, K, generator=g) * 0.02).to(torch.bfloat16)
         qa, sa = orc.quant_rows(bits(A))
-        qb, sb = orc.quant_weight_mx(bits(B), "mxfp8")
+        qb, sb = orc.quant_weight_mx(bits(B), fmt)
     return dict(m_idx=m_idx, A=qa, As=sa, B=qb, Bs=sb)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("integer_valued", [False, True])
 @pytest.mark.parametrize("counts,N,K", [([130, 0, 5, 256, 1, 300], 256, 384), ([64, 129], 384, 512)])
-def test_gemm_mxfp8_contig(orc, counts, N, K, integer_valued):
-    """FP8 activations times MX e4m3 weights (one exponent per 32 k): the
-    per-lane scale of the block-scaled MFMA; exact on integer-valued codes."""
-    announce("gemm_mxfp8_contig", counts, N, K, integer_valued)
-    ops = _mx_operands(orc, counts, N, K, seed=N + K, integer_valued=integer_valued)
-    ref = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], "mxfp8", ops["m_idx"])
+def test_gemm_mx_contig(orc, counts, N, K, integer_valued, fmt):
+    """FP8 activations times MX weights (one exponent per 32 k; e4m3, or e2m1
+    two per byte): the per-lane scale of the block-scaled MFMA; exact on
+    integer-valued codes."""
+    announce("gemm_mx_contig", fmt, counts, N, K, integer_valued)
+    ops = _mx_operands(orc, counts, N, K, seed=N + K, integer_valued=integer_valued, fmt=fmt)
+    ref = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], fmt, ops["m_idx"])
     M = len(ops["m_idx"])
     C = poison((M, N), torch.bfloat16)
-    L.grouped_gemm_contig("mxfp8", u8_dev(ops["A"]), u8_dev(ops["As"].T.copy()), u8_dev(ops["B"]),
+    L.grouped_gemm_contig(fmt, u8_dev(ops["A"]), u8_dev(ops["As"].T.copy()), u8_dev(ops["B"]),
                           u8_dev(_mx_tile(ops["Bs"])), C, i32_dev(ops["m_idx"]))
     torch.cuda.synchronize()
     got = bits(C)
@@ -333,19 +338,20 @@ def test_gemm_mxfp8_contig(orc, counts, N, K, integer_valued):
         _check_close(got, ref, valid, 2e-2, True)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("expected_m", [0, 8])
-def test_gemm_mxfp8_masked(orc, expected_m):
-    announce("gemm_mxfp8_masked", expected_m)
+def test_gemm_mx_masked(orc, expected_m, fmt):
+    announce("gemm_mx_masked", fmt, expected_m)
     G, max_m, N, K = 5, 200, 256, 384
     masked = np.array([0, 1, 200, 37, 130], np.int32)
-    ops = _mx_operands(orc, [max_m] * G, N, K, seed=31, integer_valued=True)
+    ops = _mx_operands(orc, [max_m] * G, N, K, seed=31, integer_valued=True, fmt=fmt)
     rg = orc.masked_row_group(masked, max_m)
     A = ops["A"][: G * max_m]
     As = ops["As"][: G * max_m]
-    ref = orc.gemm_mx_rows(A, As, ops["B"], ops["Bs"], "mxfp8", rg)
+    ref = orc.gemm_mx_rows(A, As, ops["B"], ops["Bs"], fmt, rg)
     C = poison((G, max_m, N), torch.bfloat16)
     As_dev = As.reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
-    L.grouped_gemm_masked("mxfp8", u8_dev(A).view(G, max_m, K), u8_dev(As_dev), u8_dev(ops["B"]),
+    L.grouped_gemm_masked(fmt, u8_dev(A).view(G, max_m, K), u8_dev(As_dev), u8_dev(ops["B"]),
                           u8_dev(_mx_tile(ops["Bs"])), C, i32_dev(masked), expected_m)
     torch.cuda.synchronize()
     got = bits(C).reshape(G * max_m, N)
@@ -353,30 +359,31 @@ def test_gemm_mxfp8_masked(orc, expected_m):
     assert np.array_equal(got[valid], ref[valid])
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("out_fp8", [False, True])
-def test_gemm_mxfp8_silu_fused_matches_separate(orc, out_fp8):
+def test_gemm_mx_silu_fused_matches_separate(orc, out_fp8, fmt):
     """MX weights through the fused w13 + SiLU-and-mul epilogue (gate and up
     scale slots) equal the plain MX GEMM followed by silu_and_mul, bit for bit."""
-    announce("gemm_mxfp8_silu", out_fp8)
+    announce("gemm_mx_silu", fmt, out_fp8)
     I, K = 256, 384
-    ops = _mx_operands(orc, [130, 0, 5, 256, 1, 300], 2 * I, K, seed=41)
+    ops = _mx_operands(orc, [130, 0, 5, 256, 1, 300], 2 * I, K, seed=41, fmt=fmt)
     M = len(ops["m_idx"])
     m_dev = i32_dev(ops["m_idx"])
     A, As, B, Bs = u8_dev(ops["A"]), u8_dev(ops["As"].T.copy()), u8_dev(ops["B"]), u8_dev(_mx_tile(ops["Bs"]))
     gu = poison((M, 2 * I), torch.bfloat16)
-    L.grouped_gemm_contig("mxfp8", A, As, B, Bs, gu, m_dev)
+    L.grouped_gemm_contig(fmt, A, As, B, Bs, gu, m_dev)
     odt = torch.uint8 if out_fp8 else torch.bfloat16
     sep, fus = poison((M, I), odt), poison((M, I), odt)
     ss = poison((I // 128, M), torch.uint8) if out_fp8 else None
     fs = poison((I // 128, M), torch.uint8) if out_fp8 else None
     L.silu_and_mul(gu, sep, out_fp8, ss, m_indices=m_dev)
-    L.grouped_gemm_contig_silu("mxfp8", A, As, B, Bs, fus, m_dev, fs)
+    L.grouped_gemm_contig_silu(fmt, A, As, B, Bs, fus, m_dev, fs)
     torch.cuda.synchronize()
     valid = ops["m_idx"] >= 0
     assert np.array_equal(fus.view(torch.uint8).cpu().numpy()[valid], sep.view(torch.uint8).cpu().numpy()[valid])
     if out_fp8:
         assert np.array_equal(fs.cpu().numpy()[:, valid], ss.cpu().numpy()[:, valid])
-    h1 = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], "mxfp8", ops["m_idx"])
+    h1 = orc.gemm_mx_rows(ops["A"], ops["As"], ops["B"], ops["Bs"], fmt, ops["m_idx"])
     _check_close(bits(gu), h1, valid, 2e-2, True)
 
 

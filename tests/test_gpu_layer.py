@@ -182,24 +182,25 @@ def test_layer_fused_silu_matches_unfused(name, T, H, I, E, El, start, k, fp8, l
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("layout", ["compact", "masked"])
 @pytest.mark.parametrize("fuse", [True, False])
-def test_layer_mxfp8_weights(orc, layout, fuse):
-    """MX e4m3 weights (one exponent per 32 k of a weight row) quantised in the
-    library drive the FP8 layer like the oracle's MX weights."""
-    announce("layer_mxfp8", layout, fuse)
+def test_layer_mx_weights(orc, layout, fuse, fmt):
+    """MX weights (one exponent per 32 k of a weight row; e4m3 or e2m1)
+    quantised in the library drive the FP8 layer like the oracle's MX weights."""
+    announce("layer_mx", fmt, layout, fuse)
     T, H, I, E, k = 160, 256, 384, 16, 4
     x, logits, w13, w2 = inputs.small_case(91, T, H, I, E, k)
     layer = MoELayer(hidden=H, intermediate=I, num_experts=E, top_k=k, max_tokens=T, fp8=True,
-                     layout=layout, expected_m=T * k // E, fuse_silu=fuse, weight_format="mxfp8",
+                     layout=layout, expected_m=T * k // E, fuse_silu=fuse, weight_format=fmt,
                      device=DEV)
     layer.set_weights(w13.to(DEV), w2.to(DEV))
     out = layer(x.to(DEV), logits.to(DEV))
     torch.cuda.synchronize()
-    a, b = orc.quant_weight_mx(bits(w13), "mxfp8")
-    c, d = orc.quant_weight_mx(bits(w2), "mxfp8")
+    a, b = orc.quant_weight_mx(bits(w13), fmt)
+    c, d = orc.quant_weight_mx(bits(w2), fmt)
     assert np.array_equal(layer.w13.cpu().numpy(), a) and np.array_equal(layer.w2.cpu().numpy(), c)
     ref = orc.moe_layer(bits(x), logits.numpy(), k, expert_start=0, num_local_experts=E,
-                        layout=layout, fp8=True, max_m=T, w13q=a, w13s=b, w2q=c, w2s=d, mx="mxfp8")
+                        layout=layout, fp8=True, max_m=T, w13q=a, w13s=b, w2q=c, w2s=d, mx=fmt)
     err = rel_fro(f32(bits(out)).astype(np.float64), f32(ref["out"]))
     assert err <= 2e-2, err
