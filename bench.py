@@ -41,12 +41,14 @@ def parse():
                     help="run w13 and SiLU-and-mul as two kernels")
     ap.add_argument("--weight-format", default=None, choices=["block128", "mxfp8", "mxfp4"],
                     help="FP8 workloads: 128x128 UE8M0 weight blocks (default) or MX e4m3 weights")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="FP8 workloads: skip the extra MX-weight timings (mxfp8, mxfp4)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
-def build_layer(wl, torch, fuse_silu=True, weight_format=None):
+def build_layer(wl, torch, fuse_silu=True, weight_format=None, make_inputs=True):
     from scatter_grouped_gemm_amd import MoELayer, inputs
     layer = MoELayer(hidden=wl.H, intermediate=wl.I, num_experts=wl.E, top_k=wl.k, max_tokens=wl.T,
                      num_local_experts=wl.El, expert_start=wl.expert_start, fp8=wl.fp8,
@@ -60,6 +62,8 @@ def build_layer(wl, torch, fuse_silu=True, weight_format=None):
         del w13, w2
     torch.cuda.synchronize()
     log(f"weights ready for {wl.El} experts in {time.time() - t0:.1f}s")
+    if not make_inputs:
+        return layer, None, None
     x = inputs.tokens(wl, "cuda")
     logits = inputs.logits(wl, "cuda")
     return layer, x, logits
@@ -128,6 +132,43 @@ def measured_traffic(wl_name, which):
     if d.get("gemm_source_sha256") != h.hexdigest() or which not in d:
         return None
     return int(d[which]["read_bytes"] + d[which]["write_bytes"])
+
+
+def time_steps(layer, x, logits, steps, warmup, torch):
+    """Mean step time (ms) over `steps` after `warmup`, HIP events on the
+    stream the layer launches on, plus per-kernel means."""
+    for _ in range(warmup):
+        layer(x, logits)
+    torch.cuda.synchronize()
+    layer.marks = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        layer(x, logits)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kern = {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in layer.marks.items()}
+    layer.marks = None
+    return ms, kern
+
+
+def mx_variants(wl, x, logits, torch, steps=10, warmup=3):
+    """The same batch with MX expert weights (e4m3 and e2m1, one exponent per
+    32 k of a weight row), timed like the main run; reported beside it."""
+    out = {}
+    for wf in ("mxfp8", "mxfp4"):
+        layer, _, _ = build_layer(wl, torch, weight_format=wf, make_inputs=False)
+        ms, kern = time_steps(layer, x, logits, steps, warmup, torch)
+        work = gemm_work(wl, layer, torch)
+        roof = roofline(work["w13_flops"], work["w13_bytes"], kern["gemm_w13_silu"], "fp8_e4m3")
+        out[wf] = {"value": round(wl.T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                   "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+                   "w13_roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac")}}
+        log(f"{wf}: {ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+        del layer
+        torch.cuda.empty_cache()
+    return out
 
 
 def requant_weights(wl, torch, reps=5):
@@ -248,20 +289,7 @@ def main():
         del a, b
     layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused,
                                    weight_format=args.weight_format if wl.fp8 else None)
-    for _ in range(args.warmup):
-        layer(x, logits)
-    torch.cuda.synchronize()
-    layer.marks = {}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        layer(x, logits)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    kern = {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in layer.marks.items()}
-    layer.marks = None
+    ms, kern = time_steps(layer, x, logits, args.steps, args.warmup, torch)
     log(f"{ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
     work = gemm_work(wl, layer, torch)
     dtype = "fp8_e4m3" if wl.fp8 else "bf16"
@@ -299,6 +327,8 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "cpu_baseline": None,
     }
+    if wl.fp8 and not layer.mx and not args.no_mx:
+        res["mx_weights"] = mx_variants(wl, x, logits, torch)
     if wl.fp8:
         res["requant_weights"] = requant_weights(wl, torch)
         log(f"requant of w13-shaped block-FP8 weights: {res['requant_weights']['ms']:.3f} ms, "
