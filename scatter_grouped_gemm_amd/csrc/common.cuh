@@ -13,12 +13,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even; NaN stays NaN; overflow goes to inf.
+// Round to nearest even (gfx950's v_cvt_pk_bf16_f32, which the compiler
+// emits for this conversion); NaN stays NaN; overflow goes to inf.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // UE8M0 exponent of a non-negative finite group maximum: the smallest e in
@@ -64,18 +62,6 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 __device__ __forceinline__ unsigned long long ballot(bool p) { return __ballot(p); }
-
-// e4m3fn (OCP, bias 7) code -> fp32, exact: exponent field 0 holds the
-// subnormals m * 2^-9, 0x7f / 0xff are NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 24;
-  const uint32_t em = c & 0x7fu;
-  if (em == 0x7fu) return __uint_as_float(sign | 0x7fc00000u);
-  const uint32_t e = em >> 3, m = em & 7u;
-  const float v = e == 0 ? static_cast<float>(m) * (1.0f / 512.0f)
-                         : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return __uint_as_float(__float_as_uint(v) | sign);
-}
 
 // SiLU in fp32: g * 1 / (1 + e^-g), with e^-g as 2^(-g log2 e) and the
 // reciprocal from the hardware approximations (each within about one fp32 ulp),

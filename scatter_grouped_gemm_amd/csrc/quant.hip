@@ -130,11 +130,14 @@ __global__ __launch_bounds__(256) void requant_weight_kernel(const uint8_t* q_in
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint2 c = *reinterpret_cast<const uint2*>(qg + static_cast<int64_t>(b.r0 + i) * K + b.c0);
+    // exact e4m3 -> fp32 by the hardware conversion, two codes per instruction
+    const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.x), false);
+    const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.x), true);
+    const auto d2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.y), false);
+    const auto d3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c.y), true);
+    const float v[8] = {d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[i][j] = bf16_to_f32(f32_to_bf16(e4m3_to_f32((c.x >> (8 * j)) & 0xffu) * sc));
-      f[i][4 + j] = bf16_to_f32(f32_to_bf16(e4m3_to_f32((c.y >> (8 * j)) & 0xffu) * sc));
-    }
+    for (int j = 0; j < 8; ++j) f[i][j] = bf16_to_f32(f32_to_bf16(v[j] * sc));
   }
   quant_block_store(f, b, N, K, q_out, s_out);
 }
