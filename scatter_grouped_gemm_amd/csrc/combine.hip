@@ -49,8 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+      o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
     *reinterpret_cast<uint4*>(out + static_cast<int64_t>(t) * H + col) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }

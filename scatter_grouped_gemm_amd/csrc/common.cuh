@@ -18,6 +18,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+// Two values rounded to bf16 and packed (a in the low half): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 h2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+}
 
 // UE8M0 exponent of a non-negative finite group maximum: the smallest e in
 // [-126, 127] with amax <= 448 * 2^e.  448 = 1.75 * 2^8, so with

@@ -686,10 +686,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
           uint16_t* const crow_ = cg_ + static_cast<int64_t>(r_) * p.N;                          \
           _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                    \
             const f32x4_t v_ = acc[jn][im];                                                      \
-            const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                     \
-                                 (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);              \
-            const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                     \
-                                 (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);              \
+            const uint32_t lo_ = pack_bf16x2(v_[0], v_[1]);                                      \
+            const uint32_t hi_ = pack_bf16x2(v_[2], v_[3]);                                      \
             *reinterpret_cast<u32x2_t*>(crow_ + jn * 16) = u32x2_t{lo_, hi_};                    \
           }                                                                                      \
         }                                                                                        \
@@ -716,10 +714,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
             uint16_t* const orow_ = static_cast<uint16_t*>(p.C) + (c_row0 + r_) * I_ + ch0_;     \
             _Pragma("unroll") for (int h = 0; h < TH; ++h) {                                     \
               const f32x4_t v_ = act4_(im, h);                                                   \
-              const uint32_t lo_ = static_cast<uint32_t>(f32_to_bf16(v_[0])) |                   \
-                                   (static_cast<uint32_t>(f32_to_bf16(v_[1])) << 16);            \
-              const uint32_t hi_ = static_cast<uint32_t>(f32_to_bf16(v_[2])) |                   \
-                                   (static_cast<uint32_t>(f32_to_bf16(v_[3])) << 16);            \
+              const uint32_t lo_ = pack_bf16x2(v_[0], v_[1]);                                    \
+              const uint32_t hi_ = pack_bf16x2(v_[2], v_[3]);                                    \
               *reinterpret_cast<u32x2_t*>(orow_ + h * 16) = u32x2_t{lo_, hi_};                   \
             }                                                                                    \
           }                                                                                      \
