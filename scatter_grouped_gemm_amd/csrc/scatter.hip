@@ -165,6 +165,104 @@ __global__ __launch_bounds__(256) void scatter_rank_kernel(
   }
 }
 
+// Steps 1-3 in one workgroup for small batches (one launch instead of three):
+// wavefront w counts, then ranks, the w-th sixteenth of the assignments;
+// thread e scans expert e's per-wavefront counts and the padded expert sizes.
+// Ranks are the same as the chunked kernels': a row's rank is the number of
+// earlier assignments (in t*k + j order) of its expert.
+constexpr int kSmallWaves = 16;
+constexpr int64_t kSmallA = 16384;  // assignments handled by the one-workgroup path
+
+template <bool MASKED>
+__global__ __launch_bounds__(1024) void scatter_front_small_kernel(
+    const int32_t* __restrict__ ids, int A, int expert_start, int El, int block_e, int max_m,
+    int32_t* __restrict__ start, int32_t* __restrict__ total, int32_t* __restrict__ start_out,
+    int32_t* __restrict__ valid_out, int32_t* __restrict__ src2dst, int32_t* __restrict__ err) {
+  extern __shared__ int lds_i[];
+  int* const cnt = lds_i;                          // [kSmallWaves][El]
+  int* const scan = lds_i + kSmallWaves * El;      // [1024]
+  int* const st_l = scan + 1024;                   // [El]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int per = (A + kSmallWaves * 64 - 1) / (kSmallWaves * 64) * 64;
+  const int a0 = w * per, a1 = a0 + per < A ? a0 + per : A;
+  if (tid == 0) *err = 0;
+  for (int i = tid; i < kSmallWaves * El; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  for (int a = a0 + lane; a < a1; a += 64) {
+    const int e = ids[a] - expert_start;
+    if (e >= 0 && e < El) atomicAdd(&cnt[w * El + e], 1);
+  }
+  __syncthreads();
+  int run = 0;
+  if (tid < El) {
+    for (int q = 0; q < kSmallWaves; ++q) {
+      const int v = cnt[q * El + tid];
+      cnt[q * El + tid] = run;
+      run += v;
+    }
+  }
+  const int padded = tid < El ? (run + block_e - 1) / block_e * block_e : 0;
+  scan[tid] = padded;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < El) {
+    const int st = scan[tid] - padded;
+    st_l[tid] = st;
+    start[tid] = st;
+    total[tid] = run;
+    if (start_out) start_out[tid] = st;
+    if (valid_out) valid_out[tid] = MASKED && run > max_m ? max_m : run;
+  }
+  __syncthreads();
+  int* const base = cnt + w * El;
+  if (!MASKED)
+    for (int e = lane; e < El; e += 64) base[e] += st_l[e];
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int bits = 32 - __clz(El);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int s0 = a0; s0 < a1; s0 += 64) {
+    const int a = s0 + lane;
+    const bool valid = a < a1;
+    const int e = valid ? ids[a] - expert_start : -1;
+    const bool local = valid && e >= 0 && e < El;
+    const int key = local ? e : El;
+    uint64_t mask = ballot(true);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(mask & below);
+    const int cnt_e = __popcll(mask);
+    int r = 0;
+    if (local) r = base[key] + rank;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (local && rank == 0) base[key] = r + cnt_e;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      int out = -1;
+      if (local) {
+        if (!MASKED) {
+          out = r;
+        } else if (r < max_m) {
+          out = key * max_m + r;
+        } else {
+          atomicOr(err, MOE_DEVERR_MASKED_OVERFLOW);
+        }
+      }
+      src2dst[a] = out;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_m_indices_kernel(const int32_t* __restrict__ start,
                                                              const int32_t* __restrict__ total,
                                                              int El, int64_t R,
@@ -295,6 +393,24 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
                             int32_t block_e, const ScatterWs& w, int32_t* start_out,
                             int32_t* valid_out, bool masked, int32_t max_m, int32_t* src2dst,
                             hipStream_t s) {
+  if (A <= kSmallA) {
+    const size_t lds = (static_cast<size_t>(kSmallWaves) * El + 1024 + El) * sizeof(int);
+    static bool attr_set[2] = {false, false};
+    auto kern = masked ? scatter_front_small_kernel<true> : scatter_front_small_kernel<false>;
+    if (!attr_set[masked ? 1 : 0]) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>((static_cast<size_t>(kSmallWaves) + 1) * 1024 * sizeof(int) +
+                                               1024 * sizeof(int))) != hipSuccess)
+        return MOE_EDEVICE;
+      attr_set[masked ? 1 : 0] = true;
+    }
+    kern<<<1, 1024, lds, s>>>(ids, static_cast<int>(A), expert_start, El, masked ? 1 : block_e,
+                              masked ? max_m : 0, w.start, w.total, start_out, valid_out, src2dst,
+                              w.err);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   const int C = static_cast<int>(num_chunks(A));
   const int nb = (C + 3) / 4;
   const size_t lds = static_cast<size_t>(4) * El * sizeof(int);
