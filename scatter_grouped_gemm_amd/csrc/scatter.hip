@@ -85,11 +85,18 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
   const int e = threadIdx.x;
   int64_t run = 0;
   if (e < El) {
-    for (int c = 0; c < C; ++c) {
-      const int64_t i = static_cast<int64_t>(c) * El + e;
-      const int v = counts[i];
-      counts[i] = static_cast<int32_t>(run);
-      run += v;
+    // 16 chunk counts in flight at a time, then their exclusive offsets
+    constexpr int B = 16;
+    for (int c0 = 0; c0 < C; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        v[j] = c0 + j < C ? counts[static_cast<int64_t>(c0 + j) * El + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j < C) counts[static_cast<int64_t>(c0 + j) * El + e] = static_cast<int32_t>(run);
+        run += v[j];
+      }
     }
   }
   const int64_t padded = e < El ? (run + block_e - 1) / block_e * block_e : 0;
