@@ -153,6 +153,30 @@ def time_steps(layer, x, logits, steps, warmup, torch):
     return ms, kern
 
 
+def graph_steps(layer, x, logits, steps, torch):
+    """The same step captured once in a HIP graph and replayed `steps` times
+    (launch overhead removed; the whole path runs in every replay)."""
+    layer(x, logits)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            layer(x, logits)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / steps
+
+
 def mx_variants(wl, x, logits, torch, steps=10, warmup=3):
     """The same batch with MX expert weights (e4m3 and e2m1, one exponent per
     32 k of a weight row), timed like the main run; reported beside it."""
@@ -290,6 +314,8 @@ def main():
     layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused,
                                    weight_format=args.weight_format if wl.fp8 else None)
     ms, kern = time_steps(layer, x, logits, args.steps, args.warmup, torch)
+    g_ms = graph_steps(layer, x, logits, args.steps, torch)
+    log(f"hip graph replay: {g_ms:.3f} ms/step")
     log(f"{ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
     work = gemm_work(wl, layer, torch)
     dtype = "fp8_e4m3" if wl.fp8 else "bf16"
@@ -325,6 +351,7 @@ def main():
                  "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),
                  "w2": w2_roof},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "hip_graph": {"ms_per_step": round(g_ms, 4), "value": round(wl.T / (g_ms * 1e-3), 1)},
         "cpu_baseline": None,
     }
     if wl.fp8 and not layer.mx and not args.no_mx:

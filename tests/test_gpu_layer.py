@@ -204,3 +204,38 @@ def test_layer_mx_weights(orc, layout, fuse, fmt):
                         layout=layout, fp8=True, max_m=T, w13q=a, w13s=b, w2q=c, w2s=d, mx=fmt)
     err = rel_fro(f32(bits(out)).astype(np.float64), f32(ref["out"]))
     assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("fp8,layout", [(True, "compact"), (True, "masked"), (False, "compact")])
+def test_layer_hip_graph_replays_match_eager(fp8, layout):
+    """The forward allocates nothing, reads nothing back and records no memset,
+    so it can be captured in a HIP graph: every replay (with new tokens copied
+    into the captured input, and eager work between replays) gives the eager
+    forward's bits."""
+    announce("layer_hip_graph", fp8, layout)
+    T, H, I, E, k = 96, 256, 256, 16, 4
+    layer = _layer(T, H, I, E, k, fp8=fp8, layout=layout, expected_m=T * k // E)
+    x0, logits0, w13, w2 = inputs.small_case(5, T, H, I, E, k)
+    layer.set_weights(w13.to(DEV), w2.to(DEV))
+    x_in = x0.to(DEV).clone()
+    l_in = logits0.to(DEV).clone()
+    layer(x_in, l_in)                                   # first launches outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            out_g = layer(x_in, l_in)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for seed in (6, 7, 8):
+        x1, l1, _, _ = inputs.small_case(seed, T, H, I, E, k)
+        x_in.copy_(x1.to(DEV))
+        l_in.copy_(l1.to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bits(out_g).copy()
+        eager = bits(layer(x_in, l_in)).copy()          # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager), seed
