@@ -144,9 +144,12 @@ __device__ __forceinline__ int tile_expert(const int32_t* m_indices, int j, int 
 // Position pos of the tile order -> expert g, M-tile mt (global index in the
 // order's M-tile space), N-tile nt and the first M-tile of the run.  Table
 // entry j describes M-tile i_lo + j: x = (first - i_lo) | (end - i_lo) << 16
-// as two int16 fields, y = the run's expert id.
+// as two int16 fields, y = the run's expert id (bits 0-23; negative for
+// padding) and, in bits 24-30, the token rows of the run's last tile minus 1
+// (every other tile of a run is full).
 struct TilePos {
   int g, mt, nt, first;
+  int rows;  // compact: rows of the tile holding tokens (the rest is padding)
 };
 // The table is read with a hand-written ds_read: the compiler orders every LDS
 // read it can see after all outstanding direct-to-LDS loads (a full vmcnt
@@ -198,6 +201,7 @@ __device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_ti
       t.nt = 0;
       t.mt = 0;
       t.first = 0;
+      t.rows = 0;
       return t;
     }
     t.g = 16 * c + c2;
@@ -206,7 +210,9 @@ __device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_ti
   } else {
     const int2 e = read_table(table, i0 - i_lo);
     const int x = __builtin_amdgcn_readfirstlane(e.x);
-    t.g = __builtin_amdgcn_readfirstlane(e.y);
+    const int y = __builtin_amdgcn_readfirstlane(e.y);
+    t.g = y < 0 ? y : (y & 0xffffff);
+    t.rows = y < 0 ? 0 : ((y >> 24) & 0x7f) + 1;  // of the run's last tile
     t.first = i_lo + static_cast<int>(static_cast<int16_t>(x & 0xffff));
     run = i_lo + (x >> 16) - t.first;
   }
@@ -215,10 +221,12 @@ __device__ __forceinline__ TilePos map_pos(const int2* table, int i_lo, int n_ti
     t.g = -1;  // an inconsistent entry is never used (cannot happen for a well-built table)
     t.nt = 0;
     t.mt = 0;
+    t.rows = 0;
     return t;
   }
   t.nt = local / run;
   t.mt = t.first + (local - t.nt * run);
+  if (MASKED || t.mt != t.first + run - 1) t.rows = 1 << 30;  // full (masked: by group size)
   return t;
 }
 
@@ -244,6 +252,7 @@ __device__ __forceinline__ void tile_rows(const GemmArgs& p, const TilePos& t, i
     row0 = static_cast<int64_t>(t.mt) * BM;
     const int64_t left = p.M - row0;
     rows = left < BM ? static_cast<int>(left) : BM;
+    rows = t.rows < rows ? t.rows : rows;  // padding rows are neither loaded nor stored
     as0 = row0;
   } else {
     const int r_in0 = (t.mt - t.first) * BM;
@@ -423,10 +432,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     if (lane < 63) after = min(after, suf_x);
     const int f0 = max(before, v[0]), f1 = max(f0, v[1]);
     const int e1 = min(after, w[1]), e0 = min(e1, w[0]);
+    // token rows of a run's last tile: its valid rows come first, so a binary
+    // search for the first padding row (-1)
+    auto last_rows = [&](int end_tile) -> int {
+      const int64_t r0 = static_cast<int64_t>(end_tile - 1) * BM;
+      int lo = 1, hi = p.M - r0 < BM ? static_cast<int>(p.M - r0) : BM;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.rowinfo[r0 + mid] >= 0) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
     if (2 * tid < R)
-      table[2 * tid] = make_int2(((f0 - i_lo) & 0xffff) | ((e0 - i_lo) << 16), id[0]);
+      table[2 * tid] = make_int2(((f0 - i_lo) & 0xffff) | ((e0 - i_lo) << 16),
+                                 id[0] < 0 ? id[0] : id[0] | ((last_rows(e0) - 1) << 24));
     if (2 * tid + 1 < R)
-      table[2 * tid + 1] = make_int2(((f1 - i_lo) & 0xffff) | ((e1 - i_lo) << 16), id[1]);
+      table[2 * tid + 1] = make_int2(((f1 - i_lo) & 0xffff) | ((e1 - i_lo) << 16),
+                                     id[1] < 0 ? id[1] : id[1] | ((last_rows(e1) - 1) << 24));
   }
   __syncthreads();  // table complete; stage memory is free
 
@@ -857,6 +880,7 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   const int64_t m_tiles = (a.M + BM - 1) / BM;
   const int64_t order_m = (MASKED ? a.G : 1) * m_tiles;
   if (!MASKED && order_m > 8 * (kRunMax - 2)) return MOE_EUNSUPPORTED;
+  if (!MASKED && a.G >= (1 << 24)) return MOE_EUNSUPPORTED;  // expert ids share a table word
   if (MASKED && a.G > kMaxMaskedGroups) return MOE_EUNSUPPORTED;
   a.n_tiles = EPI == kEpiPlain ? a.N / BN : a.N / 256;
   a.m_tiles = static_cast<int>(m_tiles);
@@ -866,12 +890,15 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   constexpr int lds = gemm_lds_bytes<BM, BN, WF, EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = grouped_gemm_kernel<BM, BN, WF, MASKED, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic-LDS limit is raised once per device the kernel runs on
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
+  if (!attr_set[dev]) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
       return MOE_EDEVICE;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   const int grid = persistent_grid();
   if (grid == 0) return MOE_EDEVICE;

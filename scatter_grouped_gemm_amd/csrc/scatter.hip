@@ -402,15 +402,17 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
                             hipStream_t s) {
   if (A <= kSmallA) {
     const size_t lds = (static_cast<size_t>(kSmallWaves) * El + 1024 + El) * sizeof(int);
-    static bool attr_set[2] = {false, false};
+    static bool attr_set[64][2] = {};  // per device, per layout
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
     auto kern = masked ? scatter_front_small_kernel<true> : scatter_front_small_kernel<false>;
-    if (!attr_set[masked ? 1 : 0]) {
+    if (!attr_set[dev][masked ? 1 : 0]) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>((static_cast<size_t>(kSmallWaves) + 1) * 1024 * sizeof(int) +
                                                1024 * sizeof(int))) != hipSuccess)
         return MOE_EDEVICE;
-      attr_set[masked ? 1 : 0] = true;
+      attr_set[dev][masked ? 1 : 0] = true;
     }
     kern<<<1, 1024, lds, s>>>(ids, static_cast<int>(A), expert_start, El, masked ? 1 : block_e,
                               masked ? max_m : 0, w.start, w.total, start_out, valid_out, src2dst,

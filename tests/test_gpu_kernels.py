@@ -500,6 +500,30 @@ def test_gemm_contig_wide_padding(orc, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_contig_blocks_padded_inside_a_run(orc, fp8):
+    """The layout contract only asks each 128-row block to hold one expert with
+    its valid rows first: an expert may pad a block and continue in the next
+    one, and the same expert may reappear later.  Every valid row is computed
+    (rows of a run's last block past its tokens are skipped)."""
+    announce("gemm_contig_padded_runs", fp8)
+    N, K = 256, 256
+    ops = _gemm_operands(orc, fp8, [384, 384, 384], N, K, seed=29, integer_valued=True, extra_rows=128)
+    m = np.full(len(ops["m_idx"]), -1, np.int32)
+    m[0:100] = 0        # expert 0: a padded block ...
+    m[128:256] = 0      # ... then a full one in the same run
+    m[256:300] = 0      # ... and a short last block
+    m[384:512] = 1      # expert 1: one full block
+    m[640:650] = 0      # expert 0 again, later
+    m[768:770] = 2      # expert 2: 2 rows; a block of padding follows
+    ops["m_idx"] = m
+    ref = _ref_gemm(orc, fp8, ops)
+    got = _run_contig(fp8, ops, N)
+    valid = m >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[_skipped_rows_contig(m)] == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_gemm_contig_integer_exact(orc, fp8):
     """Integer-valued operands make every partial sum exact, so the GPU must
     reproduce the oracle bit for bit whatever its accumulation order; a
