@@ -524,6 +524,21 @@ def test_gemm_contig_blocks_padded_inside_a_run(orc, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_contig_thousands_of_short_runs(orc, fp8):
+    """3000 experts of 1..3 rows: every run is one tile, and the 3001 M-tiles
+    spread over the eight XCD shares' run tables."""
+    announce("gemm_contig_short_runs", fp8)
+    rng = np.random.default_rng(7)
+    counts = rng.integers(1, 4, 3000).tolist()
+    N, K = 128, 256
+    ops = _gemm_operands(orc, fp8, counts, N, K, seed=31, integer_valued=True)
+    ref = _ref_gemm(orc, fp8, ops)
+    got = _run_contig(fp8, ops, N)
+    valid = ops["m_idx"] >= 0
+    assert np.array_equal(got[valid], ref[valid])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_gemm_contig_integer_exact(orc, fp8):
     """Integer-valued operands make every partial sum exact, so the GPU must
     reproduce the oracle bit for bit whatever its accumulation order; a
