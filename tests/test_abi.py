@@ -143,3 +143,26 @@ def test_empty_calls_are_no_ops():
     assert lib.grouped_gemm_contig_silu(0, FAKE, None, FAKE, None, 0, FAKE, None, None, 0, 128, 256, 2,
                                         None) == L.MOE_OK
     assert lib.moe_combine(None, 0, None, None, 0, 2, 256, None, None) == L.MOE_OK
+
+
+def test_layer_layout_choice_on_host():
+    """The layer's layout follows the measured policy ("auto"), the pages' rule
+    ("rule") or the caller; deciding it needs no GPU (buffers on the host)."""
+    from scatter_grouped_gemm_amd import MoELayer
+
+    def layer(T, E, El, layout, **kw):
+        return MoELayer(hidden=128, intermediate=128, num_experts=E, top_k=2, max_tokens=T,
+                        num_local_experts=El, layout=layout, device="cpu", **kw)
+
+    assert layer(256, 256, 32, "auto").layout == "masked"
+    assert layer(4096, 256, 32, "auto").layout == "compact"
+    assert layer(256, 8, 8, "auto").layout == "masked"          # measured: small batch
+    assert layer(256, 8, 8, "rule").layout == "compact"          # pages: all experts local
+    assert layer(4096, 256, 32, "rule").layout == "masked"
+    assert layer(64, 16, 16, "compact").layout == "compact"
+    with pytest.raises(ValueError):
+        layer(64, 16, 16, "diagonal")
+    with pytest.raises(ValueError):
+        layer(64, 16, 16, "auto", fp8=False, weight_format="mxfp8")   # MX needs the FP8 path
+    with pytest.raises(ValueError):
+        layer(64, 16, 16, "auto", fp8=True, weight_format="nvfp4")
