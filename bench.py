@@ -93,7 +93,11 @@ def gemm_work(wl, layer, torch):
     w13_out = (I * (ab + asc)) if layer.fuse_silu else (2 * I * 2)
     w13_bytes = active * 2 * I * H * (wb + sc) + A * H * (ab + asc) + A * w13_out
     w2_bytes = active * H * I * (wb + sc) + A * I * (ab + asc) + A * H * 2
+    # rows of the tiles the GEMMs execute (whole tiles, padding included)
+    bm = 64 if layer.layout == "masked" and 0 < layer.expected_m <= 64 else 128
+    rows_exec = int(((counts + bm - 1) // bm * bm).sum())
     return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
+                exec_flops=2.0 * rows_exec * (2 * I * H + H * I),
                 w13_bytes=w13_bytes, w2_bytes=w2_bytes)
 
 
@@ -134,23 +138,47 @@ def measured_traffic(wl_name, which):
     return int(d[which]["read_bytes"] + d[which]["write_bytes"])
 
 
-def time_steps(layer, x, logits, steps, warmup, torch):
+def time_steps(layer, x, logits, steps, warmup, torch, per_step=None):
     """Mean step time (ms) over `steps` after `warmup`, HIP events on the
-    stream the layer launches on, plus per-kernel means."""
+    stream the layer launches on, plus per-kernel means; `per_step` (a list)
+    receives each step's time from an event recorded between steps."""
     for _ in range(warmup):
         layer(x, logits)
     torch.cuda.synchronize()
     layer.marks = {}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
         layer(x, logits)
-    end.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    if per_step is not None:
+        per_step.extend(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     kern = {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in layer.marks.items()}
     layer.marks = None
     return ms, kern
+
+
+def memory_kernels(wl, layer, kern, work):
+    """Algorithmic HBM bytes and rate of the memory-bound kernels: scatter
+    (per assignment 2H/k read + H*b + H/128 + 8 written), combine (per token
+    2H*k + 2H + 8k) and, when run separately, SiLU-and-mul (per valid row 4I
+    read + I*b (+ I/128) written)."""
+    H, I, k = wl.H, wl.I, wl.k
+    A, T = work["assignments"], wl.T
+    b = 1 if wl.fp8 else 2
+    sc = (1.0 / 128) if wl.fp8 else 0.0
+    out = {}
+    nbytes = {"scatter": A * (2 * H / k + H * b + H * sc + 8), "combine": T * (2 * H * k + 2 * H + 8 * k)}
+    if "silu_and_mul" in kern:
+        nbytes["silu_and_mul"] = A * (4 * I + I * b + I * sc)
+    for name, nb in nbytes.items():
+        if name in kern and kern[name] > 0:
+            gbs = nb / (kern[name] * 1e-3) / 1e9
+            out[name] = {"bytes": int(nb), "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def graph_steps(layer, x, logits, steps, torch):
@@ -313,7 +341,10 @@ def main():
         del a, b
     layer, x, logits = build_layer(wl, torch, fuse_silu=not args.unfused,
                                    weight_format=args.weight_format if wl.fp8 else None)
-    ms, kern = time_steps(layer, x, logits, args.steps, args.warmup, torch)
+    per_step = []
+    ms, kern = time_steps(layer, x, logits, args.steps, args.warmup, torch, per_step)
+    q = sorted(per_step)
+    pct = {p: q[min(len(q) - 1, int(round(p / 100 * (len(q) - 1))))] for p in (10, 50, 90)}
     g_ms = graph_steps(layer, x, logits, args.steps, torch)
     log(f"hip graph replay: {g_ms:.3f} ms/step")
     log(f"{ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
@@ -337,6 +368,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_p10_p50_p90": [round(pct[10], 4), round(pct[50], 4), round(pct[90], 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -348,9 +380,11 @@ def main():
                    "silu_fused_into_w13": layer.fuse_silu, "weight_format": layer.weight_format},
         "roofline": roof,
         "gemm": {"tflops_both": round(gemm_tflops, 1),
+                 "executed_tflops_both": round(work["exec_flops"] / (gemm_ms * 1e-3) / 1e12, 1),
                  "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),
                  "w2": w2_roof},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "memory_kernels": memory_kernels(wl, layer, kern, work),
         "hip_graph": {"ms_per_step": round(g_ms, 4), "value": round(wl.T / (g_ms * 1e-3), 1)},
         "cpu_baseline": None,
     }
