@@ -43,6 +43,8 @@ def parse():
                     help="FP8 workloads: 128x128 UE8M0 weight blocks (default) or MX e4m3 weights")
     ap.add_argument("--no-mx", action="store_true",
                     help="FP8 workloads: skip the extra MX-weight timings (mxfp8, mxfp4)")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the dense vendor-library GEMMs timed for reference")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -254,6 +256,44 @@ def requant_weights(wl, torch, reps=5):
                 unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
 
 
+def vendor_dense(wl, work, torch, reps=10, warmup=3):
+    """Context, not a step of the path: the vendor library (hipBLASLt through
+    torch) on one dense GEMM of the same M x N x K as each grouped GEMM, with
+    M = the batch's valid rows and a single weight matrix.  FP8 takes one fp32
+    scale per tensor (the library has no 128x128-block UE8M0 mode), BF16 none;
+    neither has routing, padding or per-expert weights, so this is an upper
+    reference for the grouped kernels, timed on the same GPU."""
+    M, H, I = work["assignments"], wl.H, wl.I
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for name, N, K, flops in (("w13", 2 * I, H, work["w13_flops"]), ("w2", H, I, work["w2_flops"])):
+        a = torch.randn(M, K, device="cuda", generator=g)
+        w = torch.randn(N, K, device="cuda", generator=g)
+        if wl.fp8:
+            a, w = a.to(torch.float8_e4m3fn), w.to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            fn = lambda: torch._scaled_mm(a, w.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        else:
+            a, w = a.to(torch.bfloat16), w.to(torch.bfloat16)
+            fn = lambda: torch.nn.functional.linear(a, w)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        del a, w
+    out["library"] = "hipBLASLt via torch._scaled_mm (fp8, per-tensor scales)" if wl.fp8 \
+        else "hipBLASLt via torch.nn.functional.linear (bf16)"
+    return out
+
+
 def cpu_baseline(wl, x, logits, target_s, torch):
     """The oracle, as it stands, on a prefix of the same batch: routing plus the
     layout-free per-token expert path (w13 -> SiLU-mul -> (requant) -> w2 ->
@@ -394,6 +434,11 @@ def main():
         res["requant_weights"] = requant_weights(wl, torch)
         log(f"requant of w13-shaped block-FP8 weights: {res['requant_weights']['ms']:.3f} ms, "
             f"{res['requant_weights']['achieved']:.0f} GB/s")
+    if not args.no_vendor:
+        res["vendor_dense"] = vendor_dense(wl, work, torch)
+        log("dense vendor GEMMs of the same sizes: " + ", ".join(
+            f"{k} {v['ms']:.3f} ms ({v['tflops']:.0f} TFLOP/s)" for k, v in res["vendor_dense"].items()
+            if isinstance(v, dict)))
     if not args.no_cpu_baseline and not layer.mx:
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
     print(json.dumps(res), flush=True)
