@@ -14,8 +14,9 @@
 //     finishes, so a tile costs no pipeline fill or drain.  Each step waits for
 //     its stage with one vmcnt count and one barrier, then reads the next
 //     step's fragments from LDS while the current step's MFMAs run from
-//     registers.  16-byte chunks of each 128-byte LDS row are XOR-permuted so
-//     the 16 lanes of a fragment read hit distinct banks.
+//     registers; the refill's loads are spread among those MFMAs.  16-byte
+//     chunks of each 128-byte LDS row are XOR-permuted so the 16 lanes of a
+//     fragment read hit distinct banks.
 //   - MFMA: v_mfma_f32_16x16x32_bf16 for BF16 and the block-scaled
 //     v_mfma_scale_f32_16x16x128_f8f6f4 for FP8.  The UE8M0 bytes are exactly
 //     the E8M0 scales that instruction consumes; the per-128-channel activation
@@ -524,15 +525,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   do {                                                                                          \
     uint8_t* const stg_ = smem + (st_) * STAGE;                                                 \
     if constexpr (FP8) {                                                                        \
-      const uint8_t* src_;                                                                      \
-      if (wave < ASW) {                                                                         \
-        int r_ = wave * 64 + lane;                                                              \
-        r_ = r_ < d_rows ? r_ : d_rows - 1;                                                     \
-        src_ = p.A_scale + d_as0 + static_cast<int64_t>(d_k) * p.M + r_;                       \
-      } else {                                                                                  \
-        const int nb_ = lane < NB ? lane : NB - 1;                                              \
-        src_ = p.B_scale + d_bs0 + nb_ * bs_stride + d_k;                                       \
-      }                                                                                         \
+      /* both candidates computed, one selected: no branch in the step */                      \
+      int r_ = wave * 64 + lane;                                                                \
+      r_ = r_ < d_rows ? r_ : d_rows - 1;                                                       \
+      const int nb_ = lane < NB ? lane : NB - 1;                                                \
+      const uint8_t* const sa_ = p.A_scale + d_as0 + static_cast<int64_t>(d_k) * p.M + r_;     \
+      const uint8_t* const sb_ = p.B_scale + d_bs0 + nb_ * bs_stride + d_k;                     \
+      const uint8_t* const src_ = wave < ASW ? sa_ : sb_;                                       \
       if (!MX || wave < ASW) {                                                                  \
         /* wavefronts past ASW all write the same bytes into one slot */                        \
         __builtin_amdgcn_global_load_lds(src_,                                                  \
@@ -554,7 +553,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                           \
           (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);                \
     }                                                                                           \
-    /* advance; past the last tile keep re-reading its last k-step (never used) */             \
+  } while (0)
+  // Move the load side to the next k-step; past the last tile keep re-reading
+  // its last k-step (never used).
+#define MOE_ADVANCE()                                                                           \
+  do {                                                                                          \
     if (++d_k == nk) {                                                                          \
       d_k = 0;                                                                                  \
       const int np_ = next_tile<MASKED>(table, i_lo, n_tiles, used, G, d_pos + per_xcd, hi_x, per_xcd); \
@@ -806,6 +809,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   //   loads complete in issue order.
   bool c_epi = false;
   bool done = false;
+  constexpr int MPG = (KS * TM * TN) / (NVM + 1) > 0 ? (KS * TM * TN) / (NVM + 1) : 1;
 #define MOE_STEP(FC_, FN_)                                                                       \
   do {                                                                                           \
     wait_vm_lgkm0<(NST - 2) * NVM>();                                                            \
@@ -817,11 +821,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       MOE_CSET(c_next);                                                                          \
       c_next = next_tile<MASKED>(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);       \
     }                                                                                            \
-    MOE_ISSUE(st);                                                                               \
     const int st1_ = st + 1 == NST ? 0 : st + 1;                                                 \
     MOE_LOAD(FN_, st1_);                                                                         \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MOE_ISSUE(st);                                                                               \
     MOE_MMA(FC_);                                                                                \
+    /* the fragment reads first, then the refill's loads spread among the */                     \
+    /* MFMAs so that neither waits behind the other's issue               */                     \
+    __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);                                          \
+    _Pragma("unroll") for (int g_ = 0; g_ < NVM; ++g_) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);                                       \
+    }                                                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN, 0);                                \
+    /* keep the MFMAs in this block: the advance below branches */                               \
+    _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                            \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) asm volatile("" : "+v"(acc[jn][im]));    \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MOE_ADVANCE();                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     st = st1_;                                                                                   \
     if (++c_k == nk) {                                                                           \
@@ -833,7 +849,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 
   // prologue: the first NST k-steps, fully landed
 #pragma unroll
-  for (int q = 0; q < NST; ++q) MOE_ISSUE(q);
+  for (int q = 0; q < NST; ++q) {
+    MOE_ISSUE(q);
+    MOE_ADVANCE();
+  }
   wait_vm_lgkm0<0>();
   __syncthreads();
   Frags f0, f1;
@@ -849,6 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   wait_vm_lgkm0<0>();  // the trailing re-reads and the stores
 #undef MOE_DSET
 #undef MOE_ISSUE
+#undef MOE_ADVANCE
 #undef MOE_CSET
 #undef MOE_ROWOFF
 #undef MOE_LOAD
