@@ -1,13 +1,16 @@
 // Weighted combine back to token order: one workgroup per token, each thread
-// 8 consecutive channels.  Slots are summed in order j = 0..k-1 with explicit
-// round-to-nearest fp32 multiply and add (no contraction), so the result is
-// the same for a token whatever batch it arrives in.
+// 8 consecutive channels, the workgroup as wide as the row (up to 1024
+// threads; 256 for more than 8 slots, whose registers would not fit) so that
+// every slot row of a token is read in one pass.  Slots are
+// summed in order j = 0..k-1 with explicit round-to-nearest fp32 multiply and
+// add (no contraction), so the result is the same for a token whatever batch
+// it arrives in.
 #include "common.cuh"
 
 namespace moe {
 
 template <int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Y,
+__global__ __launch_bounds__(KMAX <= 8 ? 1024 : 256) void combine_kernel(const uint16_t* __restrict__ Y,
                                                       int64_t num_rows,
                                                       const int32_t* __restrict__ src2dst,
                                                       const float* __restrict__ w, int k, int H,
@@ -22,7 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     wt[threadIdx.x] = w[static_cast<int64_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  for (int col = threadIdx.x * 8; col < H; col += 256 * 8) {
+  for (int col = threadIdx.x * 8; col < H; col += blockDim.x * 8) {
     // all slot rows are loaded first (independent loads in flight), then
     // summed strictly in slot order
     uint4 v[KMAX];
@@ -64,16 +67,19 @@ extern "C" int32_t moe_combine(const void* Y, int64_t num_rows, const int32_t* s
   if (T == 0) return MOE_OK;
   if (!Y || !src2dst || !topk_weights || !out) return MOE_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // one thread per 8 channels, whole wavefronts, at most 1024
+  const int need = (H / 8 + 63) / 64 * 64;
+  const int nt = need < 1024 ? need : 1024;
   const uint16_t* y = static_cast<const uint16_t*>(Y);
   uint16_t* o = static_cast<uint16_t*>(out);
   if (k <= 2)
-    moe::combine_kernel<2><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+    moe::combine_kernel<2><<<T, nt, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
   else if (k <= 4)
-    moe::combine_kernel<4><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+    moe::combine_kernel<4><<<T, nt, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
   else if (k <= 8)
-    moe::combine_kernel<8><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+    moe::combine_kernel<8><<<T, nt, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
   else
-    moe::combine_kernel<32><<<T, 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
+    moe::combine_kernel<32><<<T, nt < 256 ? nt : 256, 0, s>>>(y, num_rows, src2dst, topk_weights, k, H, o);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -784,7 +784,8 @@ def test_silu_and_mul_fp8_and_masked(orc):
     assert np.all(qg[~v] == 0xFF)
 
 
-@pytest.mark.parametrize("T,k,H,R", [(50, 8, 7168, 500), (33, 2, 256, 80), (1, 1, 128, 3), (7, 32, 512, 300)])
+@pytest.mark.parametrize("T,k,H,R", [(50, 8, 7168, 500), (33, 2, 256, 80), (1, 1, 128, 3), (7, 32, 512, 300),
+                                       (5, 4, 16384, 40), (3, 32, 7168, 100)])
 def test_combine_bit_exact(orc, T, k, H, R):
     announce("combine", T, k, H, R)
     g = torch.Generator().manual_seed(T * k)
