@@ -801,12 +801,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // One step s (FC_ holds its fragments, read during step s-1):
   //   wait until stage s+1 (and its scales) landed and this wavefront's LDS
   //   reads are done, barrier; if step s-1 finished a tile, store it and move
-  //   the compute side on; refill the stage step s used with step s+3; read
-  //   step s+1's fragments into FN_; run step s's MFMAs.
-  //   The wait count is the number of vector memory instructions one refill
-  //   issues: those of step s+2 may still be in flight, all older ones (the
-  //   refill of step s+1, the stores) have completed because vector memory
-  //   loads complete in issue order.
+  //   the compute side on; read step s+1's fragments into FN_; refill the
+  //   stage step s used (its fragments are in FC_) with step s+NST, its loads
+  //   issued between step s's MFMAs (MPG MFMAs per load); then move the load
+  //   side on.  The reads and the refill touch different stages.
+  //   The wait count is the number of vector memory instructions of NST-2
+  //   refills: those of steps s+2 .. s+NST-1 may still be in flight, all older
+  //   ones (the refill of step s+1, the stores) have completed because vector
+  //   memory instructions complete in issue order.
   bool c_epi = false;
   bool done = false;
   constexpr int MPG = (KS * TM * TN) / (NVM + 1) > 0 ? (KS * TM * TN) / (NVM + 1) : 1;
