@@ -164,15 +164,21 @@ def time_steps(layer, x, logits, steps, warmup, torch, per_step=None):
 
 def memory_kernels(wl, layer, kern, work):
     """Algorithmic HBM bytes and rate of the memory-bound kernels: scatter
-    (per assignment 2H/k read + H*b + H/128 + 8 written), combine (per token
-    2H*k + 2H + 8k) and, when run separately, SiLU-and-mul (per valid row 4I
-    read + I*b (+ I/128) written)."""
+    (the bf16 row of every token with a local expert read once; per local
+    assignment H*b + H/128 + 8 bytes written: row, scales, row index), combine
+    (the 2H-byte rows of the local assignments read, per token a 2H-byte row
+    written and 8 bytes of weight and position per slot read) and, when run
+    separately, SiLU-and-mul (per valid row 4I read + I*b (+ I/128) written)."""
+    import torch
     H, I, k = wl.H, wl.I, wl.k
     A, T = work["assignments"], wl.T
+    local = layer.topk_ids[:T].cpu().to(torch.int64) - wl.expert_start
+    T_local = int(((local >= 0) & (local < wl.El)).any(dim=1).sum())
     b = 1 if wl.fp8 else 2
     sc = (1.0 / 128) if wl.fp8 else 0.0
     out = {}
-    nbytes = {"scatter": A * (2 * H / k + H * b + H * sc + 8), "combine": T * (2 * H * k + 2 * H + 8 * k)}
+    nbytes = {"scatter": T_local * 2 * H + A * (H * b + H * sc + 8),
+              "combine": A * 2 * H + T * (2 * H + 8 * k)}
     if "silu_and_mul" in kern:
         nbytes["silu_and_mul"] = A * (4 * I + I * b + I * sc)
     for name, nb in nbytes.items():
