@@ -483,6 +483,17 @@ def test_gemm_contig(orc, fp8, counts, N, K):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_contig_all_padding(orc, fp8):
+    """No expert has a token: every row is padding, each workgroup finds an
+    empty tile order and leaves at once, and the output is untouched."""
+    announce("gemm_contig_all_padding", fp8)
+    ops = _gemm_operands(orc, fp8, [0, 0, 0], 256, 256, seed=11)
+    assert len(ops["m_idx"]) > 0 and np.all(ops["m_idx"] < 0)
+    got = _run_contig(fp8, ops, 256)
+    assert np.all(got == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_gemm_contig_wide_padding(orc, fp8):
     """Experts padded to 384 rows leave whole M-tiles of padding between
     experts and 1000 trailing padding rows: those tiles are skipped, every

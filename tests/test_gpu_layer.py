@@ -116,6 +116,24 @@ def test_batch_invariance(fp8):
     assert np.array_equal(shuffled, full[perm.numpy()])
 
 
+@pytest.mark.parametrize("fp8,layout", [(False, "compact"), (True, "compact"), (True, "masked")])
+def test_empty_batch_then_full_batch(fp8, layout):
+    """A batch of zero tokens runs every kernel of the path on empty inputs
+    (no routed rows, all-padding layouts) and returns an empty output; the
+    next full batch is unaffected."""
+    announce("empty_batch", fp8, layout)
+    T, H, I, E, k = 64, 256, 256, 16, 4
+    x, logits, w13, w2 = inputs.small_case(55, T, H, I, E, k)
+    layer = _layer(T, H, I, E, k, fp8=fp8, layout=layout)
+    layer.set_weights(w13.to(DEV), w2.to(DEV))
+    xd, ld = x.to(DEV), logits.to(DEV)
+    before = bits(layer(xd, ld)).copy()
+    empty = layer(xd[:0].contiguous(), ld[:0].contiguous())
+    torch.cuda.synchronize()
+    assert tuple(empty.shape) == (0, H)
+    assert np.array_equal(bits(layer(xd, ld)), before)
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_uninitialised_buffers_do_not_leak(fp8):
     """Buffers are allocated uninitialised ("Support DeepGEMM for standard MoE
