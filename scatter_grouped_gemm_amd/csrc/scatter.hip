@@ -73,48 +73,75 @@ __global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __res
     for (int e = lane; e < El; e += 64) counts[static_cast<int64_t>(c) * El + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads, thread e owns expert e (El <= 1024).
-// counts become exclusive per-chunk offsets in place.
+// One workgroup of 1024 threads.  The chunk counts of expert e are split
+// into G = 1024 / El contiguous groups of chunks; thread (g, e) sums group g
+// (all of its loads in flight together), the group sums give each group's
+// base, and a second pass over the group writes the exclusive per-chunk
+// offsets in place.  Threads e < El then scan the padded expert sizes (wave
+// shuffles, then the wave totals).  El <= 1024.
 __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict__ counts, int C,
                                                             int El, int block_e, int clamp,
                                                             int32_t* __restrict__ start,
                                                             int32_t* __restrict__ total,
                                                             int32_t* __restrict__ start_out,
                                                             int32_t* __restrict__ valid_out) {
-  __shared__ int64_t sh[1024];
-  const int e = threadIdx.x;
-  int64_t run = 0;
-  if (e < El) {
-    // 16 chunk counts in flight at a time, then their exclusive offsets
-    constexpr int B = 16;
-    for (int c0 = 0; c0 < C; c0 += B) {
+  __shared__ int part[1024];
+  __shared__ int64_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = 1024 / El;
+  const int e = tid % El, g = tid / El;
+  const bool act = g < G;
+  const int cpg = (C + G - 1) / G;
+  const int c0 = g * cpg, c1 = c0 + cpg < C ? c0 + cpg : C;
+  constexpr int B = 16;
+  int sum = 0;
+  if (act) {
+    for (int cb = c0; cb < c1; cb += B) {
       int v[B];
 #pragma unroll
-      for (int j = 0; j < B; ++j)
-        v[j] = c0 + j < C ? counts[static_cast<int64_t>(c0 + j) * El + e] : 0;
+      for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? counts[static_cast<int64_t>(cb + j) * El + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) sum += v[j];
+    }
+    part[tid] = sum;
+  }
+  __syncthreads();
+  int run = 0;  // expert e's local assignments
+  if (act) {
+    int base = 0;
+    for (int q = 0; q < G; ++q) {
+      const int v = part[q * El + e];
+      if (q < g) base += v;
+      run += v;
+    }
+    for (int cb = c0; cb < c1; cb += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? counts[static_cast<int64_t>(cb + j) * El + e] : 0;
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        if (c0 + j < C) counts[static_cast<int64_t>(c0 + j) * El + e] = static_cast<int32_t>(run);
-        run += v[j];
+        if (cb + j < c1) counts[static_cast<int64_t>(cb + j) * El + e] = base;
+        base += v[j];
       }
     }
   }
-  const int64_t padded = e < El ? (run + block_e - 1) / block_e * block_e : 0;
-  sh[e] = padded;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over 1024 entries
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t v = e >= off ? sh[e - off] : 0;
-    __syncthreads();
-    sh[e] += v;
-    __syncthreads();
+  // exclusive scan of the padded sizes over the experts (threads tid < El)
+  const int64_t padded = tid < El ? static_cast<int64_t>(run + block_e - 1) / block_e * block_e : 0;
+  int64_t incl = padded;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  if (e < El) {
-    const int32_t st = static_cast<int32_t>(sh[e] - padded);
-    start[e] = st;
-    total[e] = static_cast<int32_t>(run);
-    if (start_out) start_out[e] = st;
-    if (valid_out) valid_out[e] = static_cast<int32_t>(clamp > 0 && run > clamp ? clamp : run);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) incl += wsum[q];
+  if (tid < El) {
+    const int32_t st = static_cast<int32_t>(incl - padded);
+    start[tid] = st;
+    total[tid] = run;
+    if (start_out) start_out[tid] = st;
+    if (valid_out) valid_out[tid] = static_cast<int32_t>(clamp > 0 && run > clamp ? clamp : run);
   }
 }
 

@@ -57,6 +57,12 @@ SCATTER_CASES = [
     (2000, 128, 128, 128, 0, 8, False),
     (1500, 7168, 256, 256, 0, 8, True),
     (257, 4096, 128, 128, 0, 8, False),
+    # more than 16384 assignments: the chunked count / scan / rank kernels,
+    # with the scan's chunk groups per expert uneven (20 chunks over 3
+    # groups), one group per expert, and more groups than chunks
+    (2500, 128, 300, 300, 0, 8, True),
+    (4100, 256, 1000, 700, 300, 4, False),
+    (6000, 128, 3, 3, 0, 3, False),
 ]
 
 
