@@ -17,7 +17,7 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;   // assignments per wavefront chunk
+constexpr int kChunk = 256;    // assignments per wavefront chunk
 constexpr int kWsHeader = 256;  // bytes: device error word + padding
 
 struct ScatterWs {
