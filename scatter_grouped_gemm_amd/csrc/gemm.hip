@@ -668,22 +668,77 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       }                                                                                          \
     }                                                                                            \
   } while (0)
-#define MOE_MMA(F_)                                                                              \
+// One activation fragment (k-substep ks, row block im) of stage st_.
+#define MOE_LOAD_A1(F_, st_, ks, im)                                                             \
+  do {                                                                                           \
+    const uint8_t* S_ = smem + (st_) * STAGE;                                                    \
+    const int rb_ = wm * WM + (im) * 16;                                                         \
+    if constexpr (FP8) {                                                                         \
+      const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, CK_LO));        \
+      const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, CK_HI));        \
+      F_.a[ks][im] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],                 \
+                             (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};                \
+    } else {                                                                                     \
+      F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, (ks) * 4 + frag_k));  \
+    }                                                                                            \
+  } while (0)
+// The weight fragments and the scales of stage st_.
+#define MOE_LOAD_B(F_, st_)                                                                      \
+  do {                                                                                           \
+    const uint8_t* S_ = smem + (st_) * STAGE;                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
+      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                        \
+        const int rb_ = BM + wn * WN + jn * 16;                                                  \
+        if constexpr (W4) {                                                                      \
+          const u32x4_t v_ = *reinterpret_cast<const u32x4_t*>(                                  \
+              S_ + BM * 128 + (wn * WN + jn * 16 + frag_row) * 64 + ((frag_k ^ swz4_l) << 4));   \
+          F_.b[ks][jn] = i32x8_t{(int)v_[0], (int)v_[1], (int)v_[2], (int)v_[3], 0, 0, 0, 0};    \
+        } else if constexpr (FP8) {                                                              \
+          const u32x4_t lo_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, CK_LO));    \
+          const u32x4_t hi_ = *reinterpret_cast<const u32x4_t*>(S_ + MOE_ROWOFF(rb_, CK_HI));    \
+          F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
+                                 (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
+        } else {                                                                                 \
+          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+    if constexpr (FP8) {                                                                         \
+      const uint8_t* X_ = S_ + SDATA;                                                            \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im)                                          \
+        F_.sa[im] = X_[(wm * WM + im * 16 + frag_row) * 4];                                      \
+      if constexpr (MX) {                                                                        \
+        const uint8_t* M_ = X_ + ASW * kScaleSlot + frag_k * 64 + frag_row * 4;                 \
+        F_.sw = *reinterpret_cast<const int*>(M_ + mx_c0 * kScaleSlot);                          \
+        if (EPI != kEpiPlain) F_.sw2 = *reinterpret_cast<const int*>(M_ + (mx_c0 + 2) * kScaleSlot); \
+      } else {                                                                                   \
+        F_.sw = X_[ASW * kScaleSlot + (EPI == kEpiPlain ? wblk : 0) * 4];                        \
+        F_.sw2 = X_[ASW * kScaleSlot + 4];                                                       \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+// The step's MFMAs row block by row block (FC_); once a block's MFMAs are
+// issued, its activation fragment registers take the next step's (FN_, from
+// stage st_), so the two steps' activation fragments share registers and only
+// the weight fragments are held twice.
+#define MOE_MMA_IM(FC_, FN_, st_)                                                                \
   do {                                                                                           \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                            \
-      _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                          \
-        _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                      \
+      _Pragma("unroll") for (int im = 0; im < TM; ++im) {                                        \
+        _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                      \
           if constexpr (FP8)                                                                     \
             acc[jn][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                      \
-                F_.b[ks][jn], F_.a[ks][im], acc[jn][im], W4 ? 4 : 0, 0, 0,                       \
-                MX ? (((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw) >>                   \
+                FC_.b[ks][jn], FC_.a[ks][im], acc[jn][im], W4 ? 4 : 0, 0, 0,                     \
+                MX ? (((EPI != kEpiPlain && jn >= TN / 2) ? FC_.sw2 : FC_.sw) >>                 \
                       (8 * (mx_j0 + (EPI != kEpiPlain ? jn % (TN / 2) : jn))))                    \
-                   : ((EPI != kEpiPlain && jn >= TN / 2) ? F_.sw2 : F_.sw),                      \
-                0, F_.sa[im]);                                                                   \
+                   : ((EPI != kEpiPlain && jn >= TN / 2) ? FC_.sw2 : FC_.sw),                    \
+                0, FC_.sa[im]);                                                                  \
           else                                                                                   \
-            acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F_.b[ks][jn], F_.a[ks][im],    \
+            acc[jn][im] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FC_.b[ks][jn], FC_.a[ks][im],  \
                                                                   acc[jn][im], 0, 0, 0);         \
         }                                                                                        \
+        MOE_LOAD_A1(FN_, st_, ks, im);                                                           \
+      }                                                                                          \
   } while (0)
   // Stores of the finished compute tile (lane: 4 consecutive columns of a row
   // per 16x16 block), then a fresh accumulator.
@@ -801,17 +856,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // One step s (FC_ holds its fragments, read during step s-1):
   //   wait until stage s+1 (and its scales) landed and this wavefront's LDS
   //   reads are done, barrier; if step s-1 finished a tile, store it and move
-  //   the compute side on; read step s+1's fragments into FN_; refill the
-  //   stage step s used (its fragments are in FC_) with step s+NST, its loads
-  //   issued between step s's MFMAs (MPG MFMAs per load); then move the load
-  //   side on.  The reads and the refill touch different stages.
+  //   the compute side on; read step s+1's weight fragments and scales into
+  //   FN_; refill the stage step s used (its fragments are in FC_) with step
+  //   s+NST; run step s's MFMAs row block by row block, each block followed by
+  //   the read of step s+1's activation fragment into the registers it frees,
+  //   with the refill's loads spread over the blocks; then move the load side
+  //   on.  The reads and the refill touch different stages.
   //   The wait count is the number of vector memory instructions of NST-2
   //   refills: those of steps s+2 .. s+NST-1 may still be in flight, all older
   //   ones (the refill of step s+1, the stores) have completed because vector
   //   memory instructions complete in issue order.
   bool c_epi = false;
   bool done = false;
-  constexpr int MPG = (KS * TM * TN) / (NVM + 1) > 0 ? (KS * TM * TN) / (NVM + 1) : 1;
+  // LDS reads per step: weight fragments and scales (NRB), one activation
+  // fragment (NRA); refill loads per row-block group (VPG)
+  constexpr int NRA = FP8 ? 2 : 1;
+  constexpr int NRB = KS * TN * (W4 ? 1 : (FP8 ? 2 : 1)) + (FP8 ? TM + 2 : 0);
+  constexpr int VPG = (NVM + KS * TM - 1) / (KS * TM);
 #define MOE_STEP(FC_, FN_)                                                                       \
   do {                                                                                           \
     wait_vm_lgkm0<(NST - 2) * NVM>();                                                            \
@@ -824,17 +885,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       c_next = next_tile<MASKED>(table, i_lo, n_tiles, used, G, c_pos + per_xcd, hi_x, per_xcd);       \
     }                                                                                            \
     const int st1_ = st + 1 == NST ? 0 : st + 1;                                                 \
-    MOE_LOAD(FN_, st1_);                                                                         \
+    MOE_LOAD_B(FN_, st1_);                                                                       \
     MOE_ISSUE(st);                                                                               \
-    MOE_MMA(FC_);                                                                                \
-    /* the fragment reads first, then the refill's loads spread among the */                     \
-    /* MFMAs so that neither waits behind the other's issue               */                     \
-    __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);                                          \
-    _Pragma("unroll") for (int g_ = 0; g_ < NVM; ++g_) {                                         \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
-      __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);                                       \
+    MOE_MMA_IM(FC_, FN_, st1_);                                                                  \
+    /* the weight-fragment reads first, then per row block its MFMAs with */                     \
+    /* a share of the refill's loads, then the block's next-step reads    */                     \
+    __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);                                         \
+    _Pragma("unroll") for (int g_ = 0; g_ < KS * TM; ++g_) {                                     \
+      __builtin_amdgcn_sched_group_barrier(0x020, VPG, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, NRA, 0);                                       \
     }                                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x020, NVM, 0);                                         \
     /* keep the MFMAs in this block: the advance below branches */                               \
     _Pragma("unroll") for (int jn = 0; jn < TN; ++jn)                                            \
       _Pragma("unroll") for (int im = 0; im < TM; ++im) asm volatile("" : "+v"(acc[jn][im]));    \
@@ -874,7 +936,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 #undef MOE_CSET
 #undef MOE_ROWOFF
 #undef MOE_LOAD
-#undef MOE_MMA
+#undef MOE_LOAD_A1
+#undef MOE_LOAD_B
+#undef MOE_MMA_IM
 #undef MOE_EPILOGUE
 #undef MOE_STEP
 #endif
