@@ -4,8 +4,10 @@
 // Design (gfx950, wave64, 160 KB LDS):
 //   - Persistent workgroups of 512 threads (8 wavefronts, two per SIMD), one
 //     per CU.  A tile of C is BM x BN (128 x 256; 128 x 128 when N % 256 != 0;
-//     masked tiles are 64 rows tall for small expected counts); each
+//     masked tiles are 64 or 16 rows tall for small expected counts); each
 //     wavefront owns a 64-row (or BM-row) by 64- or 32-column sub-tile.
+//     When a stage is not a whole number of 1 KB loads per wavefront (16-row
+//     tiles), the first wavefronts issue one load more and wait accordingly.
 //   - The k loop is one flat stream of k-steps over all of the workgroup's
 //     tiles.  A k-step covers 128 bytes of every tile row (64 bf16 or 128
 //     e4m3), moved from global memory straight into LDS (global_load_lds, 16
@@ -102,7 +104,7 @@ constexpr int weight_row_bytes(int wf) { return wf == kWfMxFp4 ? 64 : 128; }
 template <int BM, int BN, int WF>
 constexpr int gemm_stage_bytes() {
   return BM * 128 + BN * weight_row_bytes(WF) +
-         (WF == kWfBf16 ? 0 : (BM / 64 + (WF >= kWfMxFp8 ? BN / 64 : 1)) * kScaleSlot);
+         (WF == kWfBf16 ? 0 : ((BM + 63) / 64 + (WF >= kWfMxFp8 ? BN / 64 : 1)) * kScaleSlot);
 }
 // LDS: stages, the run table and, for the FP8 SiLU epilogue, the per-row
 // maxima of the column wavefronts.  Four stages (three in flight) where they
@@ -278,13 +280,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   constexpr int SDATA = BM * 128 + BN * BROW;            // stage data bytes
   constexpr int STAGE = gemm_stage_bytes<BM, BN, WF>();
   constexpr int NST = gemm_stages<BM, BN, WF, EPI>();     // LDS stages
-  constexpr int NLD = SDATA / (1024 * kWaves);  // 16-byte direct loads per wavefront per stage
-  constexpr int NVM = NLD + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step
+  constexpr int NLDT = SDATA / 1024;        // 16-byte direct loads per stage
+  constexpr int NLD = NLDT / kWaves;        // per wavefront; the first NLDX wavefronts one more
+  constexpr int NLDX = NLDT % kWaves;
+  constexpr int NLDM = NLD + (NLDX ? 1 : 0);
+  constexpr int NVM = NLDM + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step (at most)
   constexpr int NB = BN / 128;              // weight-scale blocks per tile
-  constexpr int ASW = BM / 64;              // wavefronts fetching activation scales
-  static_assert(BM % 64 == 0 && BN % 128 == 0 && WN <= 128 && WM % 16 == 0 && WN % 16 == 0,
-                "tile shape");
-  static_assert(SDATA % (1024 * kWaves) == 0, "stage bytes split evenly over the wavefronts");
+  constexpr int ASW = (BM + 63) / 64;       // wavefronts fetching activation scales
+  static_assert((BM % 64 == 0 || (BM == 16 && MASKED)) && BN % 128 == 0 && WN <= 128 &&
+                WM % 16 == 0 && WN % 16 == 0, "tile shape");
+  static_assert(SDATA % 1024 == 0, "stage bytes in whole direct loads");
   static_assert(ASW < kWaves, "a wavefront is left for the weight scales");
   // The SiLU epilogue takes gate block nt and up block nt into one tile, laid
   // out in the stage as chunks of CH = WN/2 rows gate, up, gate, up, ... so
@@ -299,6 +304,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // this wavefront's direct loads per stage and the first of them
+  const int nldw = NLD + (wave < NLDX ? 1 : 0);
+  const int qbase = wave * NLD + (wave < NLDX ? wave : NLDX);
   const int n_tiles = p.n_tiles;
 
   // ======== set-up: this workgroup's share of the tile order ========
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   constexpr int NMX = BN / 64;
   const int c_w = wave >= ASW ? (wave - ASW) % NMX : 0;
   int d_rows;
-  uint32_t soff[NLD];  // per-lane source offsets from the tile's A / B rows
+  uint32_t soff[NLDM];  // per-lane source offsets from the tile's A / B rows
   // A direct load moves 1 KB (64 lanes x 16 bytes) into LDS: 8 activation rows,
   // or 1024 / BROW weight rows; lane i carries the 16-byte chunk that belongs
   // at LDS position i, i.e. source chunk (i & 7) ^ swz(row) of a 128-byte row,
@@ -498,8 +506,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     } else {                                                                                  \
       d_bs0 = (static_cast<int64_t>(t_.g) * (p.N / 128) + t_.nt * (NBW / 128)) * KB;          \
     }                                                                                         \
-    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                         \
-      const int q_ = wave * NLD + j;                                                          \
+    _Pragma("unroll") for (int j = 0; j < NLDM; ++j) {                                        \
+      const int q_ = qbase + j;                                                               \
       if (q_ * 1024 < BM * 128) {                                                             \
         const int R_ = q_ * 8 + (lane >> 3);                                                  \
         const int c_ = (lane & 7) ^ lds_swz(R_);                                              \
@@ -547,11 +555,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
     }                                                                                           \
     const uint8_t* ab_ = p.A + d_aoff + static_cast<int64_t>(d_k) * 128;                        \
     const uint8_t* bb_ = p.B + d_boff + static_cast<int64_t>(d_k) * BROW;                       \
-    uint8_t* const dst_ = stg_ + wave * NLD * 1024;                                             \
-    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                           \
-      const bool is_a_ = (wave * NLD + j) * 1024 < BM * 128;                                    \
-      __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                           \
-          (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);                \
+    uint8_t* const dst_ = stg_ + qbase * 1024;                                                  \
+    _Pragma("unroll") for (int j = 0; j < NLDM; ++j) {                                          \
+      if (j < NLD || j < nldw) {                                                                \
+        const bool is_a_ = (qbase + j) * 1024 < BM * 128;                                       \
+        __builtin_amdgcn_global_load_lds((is_a_ ? ab_ : bb_) + soff[j],                         \
+            (__attribute__((address_space(3))) void*)(dst_ + j * 1024), 16, 0, 0);              \
+      }                                                                                         \
     }                                                                                           \
   } while (0)
   // Move the load side to the next k-step; past the last tile keep re-reading
@@ -875,7 +885,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   constexpr int VPG = (NVM + KS * TM - 1) / (KS * TM);
 #define MOE_STEP(FC_, FN_)                                                                       \
   do {                                                                                           \
-    wait_vm_lgkm0<(NST - 2) * NVM>();                                                            \
+    if (NLDX == 0 || wave < NLDX) wait_vm_lgkm0<(NST - 2) * NVM>();                              \
+    else wait_vm_lgkm0<(NST - 2) * (NVM - 1)>();                                                 \
     __builtin_amdgcn_s_barrier();                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     if (c_epi) {                                                                                 \
@@ -1070,6 +1081,7 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool n256 = N % 256 == 0;
   // tile height from the hint: small expected counts waste less work on 64 rows
+  if (expected_m > 0 && expected_m <= 16 && N % 256 == 0) return launch_dtype<16, 256, true>(dtype, a, s);
   if (expected_m > 0 && expected_m <= 64) {
     if (n256) return launch_dtype<64, 256, true>(dtype, a, s);
     return launch_dtype<64, 128, true>(dtype, a, s);
@@ -1148,6 +1160,10 @@ extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const 
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool q8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if (expected_m > 0 && expected_m <= 16) {
+    if (q8) return launch_dtype<16, 256, true, kEpiSiluFp8>(dtype, a, s);
+    return launch_dtype<16, 256, true, kEpiSiluBf16>(dtype, a, s);
+  }
   if (expected_m > 0 && expected_m <= 64) {
     if (q8) return launch_dtype<64, 256, true, kEpiSiluFp8>(dtype, a, s);
     return launch_dtype<64, 256, true, kEpiSiluBf16>(dtype, a, s);
