@@ -265,8 +265,8 @@ int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8_t* A_scale
 /* Masked layout, P2 key source excerpt of _BF16GroupedMaskedWarmupExecutor:
  * C[g, r, :] = A[g, r, :] . B[g]^T for r < masked_m[g].
  *   A [G][max_m][K], C [G][max_m][N]; FP8 A_scale [G][K/128][max_m].
- *   expected_m  a hint of typical masked_m (sizes tiles: 16 rows when
- *               1 <= expected_m <= 16 and N % 256 == 0, 64 rows when
+ *   expected_m  a hint of typical masked_m (sizes tiles: 16 or 32 rows when
+ *               1 <= expected_m <= 16 or <= 32 and N % 256 == 0, 64 rows when
  *               1 <= expected_m <= 64, else 128); it never changes a result.
  *               0 = no hint.
  *   Rows at or past masked_m[g] receive unspecified values, except that rows

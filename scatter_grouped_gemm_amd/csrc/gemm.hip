@@ -4,10 +4,10 @@
 // Design (gfx950, wave64, 160 KB LDS):
 //   - Persistent workgroups of 512 threads (8 wavefronts, two per SIMD), one
 //     per CU.  A tile of C is BM x BN (128 x 256; 128 x 128 when N % 256 != 0;
-//     masked tiles are 64 or 16 rows tall for small expected counts); each
+//     masked tiles are 64, 32 or 16 rows tall for small expected counts); each
 //     wavefront owns a 64-row (or BM-row) by 64- or 32-column sub-tile.
-//     When a stage is not a whole number of 1 KB loads per wavefront (16-row
-//     tiles), the first wavefronts issue one load more and wait accordingly.
+//     When a stage is not a whole number of 1 KB loads per wavefront (16- and
+//     32-row tiles), the first wavefronts issue one load more and wait accordingly.
 //   - The k loop is one flat stream of k-steps over all of the workgroup's
 //     tiles.  A k-step covers 128 bytes of every tile row (64 bf16 or 128
 //     e4m3), moved from global memory straight into LDS (global_load_lds, 16
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   constexpr int NVM = NLDM + (FP8 ? 1 : 0);  // vector memory instructions per wavefront per step (at most)
   constexpr int NB = BN / 128;              // weight-scale blocks per tile
   constexpr int ASW = (BM + 63) / 64;       // wavefronts fetching activation scales
-  static_assert((BM % 64 == 0 || (BM == 16 && MASKED)) && BN % 128 == 0 && WN <= 128 &&
+  static_assert((BM % 64 == 0 || ((BM == 16 || BM == 32) && MASKED)) && BN % 128 == 0 && WN <= 128 &&
                 WM % 16 == 0 && WN % 16 == 0, "tile shape");
   static_assert(SDATA % 1024 == 0, "stage bytes in whole direct loads");
   static_assert(ASW < kWaves, "a wavefront is left for the weight scales");
@@ -1082,6 +1082,7 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   const bool n256 = N % 256 == 0;
   // tile height from the hint: small expected counts waste less work on 64 rows
   if (expected_m > 0 && expected_m <= 16 && N % 256 == 0) return launch_dtype<16, 256, true>(dtype, a, s);
+  if (expected_m > 0 && expected_m <= 32 && N % 256 == 0) return launch_dtype<32, 256, true>(dtype, a, s);
   if (expected_m > 0 && expected_m <= 64) {
     if (n256) return launch_dtype<64, 256, true>(dtype, a, s);
     return launch_dtype<64, 128, true>(dtype, a, s);
@@ -1163,6 +1164,10 @@ extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const 
   if (expected_m > 0 && expected_m <= 16) {
     if (q8) return launch_dtype<16, 256, true, kEpiSiluFp8>(dtype, a, s);
     return launch_dtype<16, 256, true, kEpiSiluBf16>(dtype, a, s);
+  }
+  if (expected_m > 0 && expected_m <= 32) {
+    if (q8) return launch_dtype<32, 256, true, kEpiSiluFp8>(dtype, a, s);
+    return launch_dtype<32, 256, true, kEpiSiluBf16>(dtype, a, s);
   }
   if (expected_m > 0 && expected_m <= 64) {
     if (q8) return launch_dtype<64, 256, true, kEpiSiluFp8>(dtype, a, s);

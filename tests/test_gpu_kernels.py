@@ -571,7 +571,7 @@ def test_gemm_contig_integer_exact(orc, fp8):
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("integer_valued", [False, True])
 def test_gemm_masked_all_tile_heights(orc, fp8, integer_valued):
-    """Masked layout; every expected_m hint (tile heights 16, 64 and 128) gives the
+    """Masked layout; every expected_m hint (tile heights 16, 32, 64 and 128) gives the
     same bits, equal to the oracle (exact for integer-valued operands)."""
     announce("gemm_masked", fp8, integer_valued)
     G, max_m, N, K = 5, 200, 256, 384
@@ -584,7 +584,7 @@ def test_gemm_masked_all_tile_heights(orc, fp8, integer_valued):
     else:
         ref = orc.gemm_bf16_rows(A, ops["B"], rg)
     outs = []
-    for em in (0, 8, 50, 200):
+    for em in (0, 8, 24, 50, 200):
         C = poison((G, max_m, N), torch.bfloat16)
         if fp8:
             As = ops["As"][: G * max_m].reshape(G, max_m, K // 128).transpose(0, 2, 1).copy()
