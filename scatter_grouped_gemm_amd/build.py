@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 OBJDIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "scatter.hip", "quant.hip", "combine.hip", "gemm.hip"]
+SOURCES = ["route.hip", "scatter.hip", "quant.hip", "combine.hip", "gemm.hip", "gemm_wreg.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

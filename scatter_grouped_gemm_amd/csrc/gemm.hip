@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "common.cuh"
+#include "gemm_wreg.h"
 
 namespace moe {
 
@@ -1054,6 +1055,11 @@ extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if ((fp8 || dtype == MOE_DTYPE_BF16) && wreg_supported(M, N, K, G, fp8)) {
+    WregArgs w{a.A, a.A_scale, a.B, a.B_scale, C, nullptr, m_indices, M, N, K, G};
+    return launch_wreg(w, fp8, kWrEpiPlain, s);
+  }
   if (N % 256 == 0) return launch_dtype<128, 256, false>(dtype, a, s);
   return launch_dtype<128, 128, false>(dtype, a, s);
 }
@@ -1128,6 +1134,11 @@ extern "C" int32_t grouped_gemm_contig_silu(int32_t dtype, const void* A, const 
   a.K = K;
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  if ((fp8 || dtype == MOE_DTYPE_BF16) && wreg_supported(M, 2 * I, K, G, fp8)) {
+    WregArgs w{a.A, a.A_scale, a.B, a.B_scale, out, out_scale, m_indices, M, 2 * I, K, G};
+    return launch_wreg(w, fp8, out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0 ? kWrEpiSiluFp8 : kWrEpiSiluBf16, s);
+  }
   if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
     return launch_dtype<128, 256, false, kEpiSiluFp8>(dtype, a, s);
   return launch_dtype<128, 256, false, kEpiSiluBf16>(dtype, a, s);
