@@ -50,6 +50,7 @@
 //     every tile size and layout; a row's result depends only on its own A row
 //     and its expert's weights.
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "common.cuh"
@@ -958,16 +959,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 
 // Persistent grid: one workgroup per CU (the LDS footprint allows no more),
 // rounded down to a multiple of the 8 XCDs.
+// Workgroups of the persistent grid: the CU count rounded down to a multiple
+// of the 8 XCDs, looked up once per device (thread-safe).
 static int persistent_grid() {
+  static std::once_flag once[64];
   static int grid[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (grid[dev] == 0) {
+  std::call_once(once[dev], [dev]() {
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    grid[dev] = cus >= 8 ? cus / 8 * 8 : 8;
-  }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      grid[dev] = cus >= 8 ? cus / 8 * 8 : 8;
+  });
   return grid[dev];
 }
 
@@ -988,16 +991,16 @@ int32_t launch_gemm(GemmArgs a, hipStream_t s) {
   constexpr int lds = gemm_lds_bytes<BM, BN, WF, EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = grouped_gemm_kernel<BM, BN, WF, MASKED, EPI>;
-  // the dynamic-LDS limit is raised once per device the kernel runs on
-  static bool attr_set[64] = {};
+  // the dynamic-LDS limit is raised once per device the kernel runs on (thread-safe)
+  static std::once_flag once[64];
+  static bool attr_ok[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
-  if (!attr_set[dev]) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-      return MOE_EDEVICE;
-    attr_set[dev] = true;
-  }
+  std::call_once(once[dev], [dev, kern]() {
+    attr_ok[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+  });
+  if (!attr_ok[dev]) return MOE_EDEVICE;
   const int grid = persistent_grid();
   if (grid == 0) return MOE_EDEVICE;
   kern<<<grid, kThreads, lds, s>>>(a);

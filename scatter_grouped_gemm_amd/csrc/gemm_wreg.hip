@@ -162,19 +162,25 @@ __device__ __forceinline__ void mma_block(f32x4 (&c)[4], const typename FragT<FP
 
 // The accumulators live in AGPRs and only assembly writes them: these two
 // helpers are the only other accesses.  acc_zero clears the four tiles of a
-// row block with 4x4x4 MFMAs of zero operands and a zero C (two passes each);
-// acc_read copies them into VGPRs at this point of the program (the tie makes
-// the compiler emit the copies here rather than hoisting all 256 of them).
+// row block with 4x4x4 MFMAs of zero operands and a zero C (two passes each).
+// The zero operand is written inside the statement, followed by the wait
+// states a VALU write needs before an MFMA reads it: the compiler's hazard
+// recognizer does not see MFMAs inside assembly, so a zero register it
+// materialised just before the statement could be read while still being
+// written.  acc_read copies them into VGPRs at this point of the program (the
+// tie makes the compiler emit the copies here rather than hoisting all 256 of
+// them).
 __device__ __forceinline__ void acc_zero(f32x4 (&c)[4]) {
   typedef __attribute__((ext_vector_type(2))) int i32x2;
-  const i32x2 z = {0, 0};
+  i32x2 z;
   asm volatile(
+      "v_mov_b64 %4, 0\n\t"
+      "s_nop 4\n\t"
       "v_mfma_f32_4x4x4_16b_f16 %0, %4, %4, 0\n\t"
       "v_mfma_f32_4x4x4_16b_f16 %1, %4, %4, 0\n\t"
       "v_mfma_f32_4x4x4_16b_f16 %2, %4, %4, 0\n\t"
       "v_mfma_f32_4x4x4_16b_f16 %3, %4, %4, 0"
-      : "=a"(c[0]), "=a"(c[1]), "=a"(c[2]), "=a"(c[3])
-      : "v"(z));
+      : "=a"(c[0]), "=a"(c[1]), "=a"(c[2]), "=a"(c[3]), "=&v"(z));
 }
 __device__ __forceinline__ void acc_read(const f32x4 (&c)[4], f32x4 (&o)[4]) {
   asm volatile("" : "=v"(o[0]), "=v"(o[1]), "=v"(o[2]), "=v"(o[3]) : "0"(c[0]), "1"(c[1]), "2"(c[2]), "3"(c[3]));
@@ -728,6 +734,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       c_k = 0;
       const Tile cn = c_next();
       mfma_drain();
+      // the accumulator copies of the epilogue stay after the drain
+      __builtin_amdgcn_sched_barrier(0);
       epilogue();
       done = cn.rows <= 0;
       ct = cn;

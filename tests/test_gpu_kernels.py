@@ -568,6 +568,87 @@ def test_gemm_contig_integer_exact(orc, fp8):
     assert np.array_equal(got[valid], ref[valid])
 
 
+def _many_tiles_layout(seed, nblocks=400, G=16):
+    """m_indices of `nblocks` 128-row blocks cycling over G experts, each with
+    1..24 valid rows, and every 40th run three blocks long: with 256
+    persistent workgroups each one processes three or more tiles, so every
+    tile after a workgroup's first starts from accumulators cleared by the
+    previous tile's epilogue."""
+    rng = np.random.default_rng(seed)
+    m, j = [], 0
+    while j < nblocks:
+        e = j % G
+        if j % 40 == 39:
+            c = 256 + int(rng.integers(1, 129))
+            nb = 3
+        else:
+            c = int(rng.integers(1, 25))
+            nb = 1
+        m += [e] * c + [-1] * (nb * 128 - c)
+        j += nb
+    m += [-1] * 128
+    return np.array(m, np.int32)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_contig_many_tiles_per_workgroup(orc, fp8):
+    """Several tiles per workgroup (the full-size case) with a k loop whose
+    length is not a multiple of the kernel's stage count: integer-valued
+    operands, bit-exact against the oracle on every valid row."""
+    announce("gemm_contig_many_tiles", fp8)
+    N, K = 512, 384
+    m = _many_tiles_layout(41)
+    G = 16
+    ops = _gemm_operands(orc, fp8, [1] * G, N, K, seed=43, integer_valued=True, extra_rows=len(m) - 128 * G)
+    ops["m_idx"] = m
+    assert len(ops["A"]) == len(m)
+    ref = _ref_gemm(orc, fp8, ops)
+    got = _run_contig(fp8, ops, N)
+    valid = m >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[_skipped_rows_contig(m)] == 0xFFFF)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("out_fp8", [False, True])
+def test_gemm_silu_fused_many_tiles_per_workgroup(orc, fp8, out_fp8):
+    """The fused SiLU epilogue with several tiles per workgroup equals the
+    plain GEMM followed by silu_and_mul bit for bit on every valid row."""
+    announce("gemm_silu_many_tiles", fp8, out_fp8)
+    I, K = 256, 384
+    m = _many_tiles_layout(47)
+    G = 16
+    ops = _gemm_operands(orc, fp8, [1] * G, 2 * I, K, seed=53, extra_rows=len(m) - 128 * G)
+    M = len(m)
+    m_dev = i32_dev(m)
+    if fp8:
+        A, As = u8_dev(ops["A"]), u8_dev(ops["As"].T.copy())
+        B, Bs = u8_dev(ops["B"]), u8_dev(ops["Bs"])
+    else:
+        A, As, B, Bs = to_dev_bf16(ops["A"]), None, to_dev_bf16(ops["B"]), None
+    C = poison((M, 2 * I), torch.bfloat16)
+    L.grouped_gemm_contig(fp8, A, As, B, Bs, C, m_dev)
+    odt = torch.uint8 if out_fp8 else torch.bfloat16
+    sep = poison((M, I), odt)
+    sep_s = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    L.silu_and_mul(C, sep, out_fp8, sep_s, m_indices=m_dev)
+    fused = poison((M, I), odt)
+    fused_s = poison((I // 128, M), torch.uint8) if out_fp8 else None
+    L.grouped_gemm_contig_silu(fp8, A, As, B, Bs, fused, m_dev, fused_s)
+    torch.cuda.synchronize()
+    v = torch.from_numpy(m >= 0)
+    a, b = fused.cpu(), sep.cpu()
+    if not out_fp8:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    assert torch.equal(a[v], b[v])
+    if out_fp8:
+        assert np.array_equal(fused_s.cpu().numpy()[:, m >= 0], sep_s.cpu().numpy()[:, m >= 0])
+    # and the plain product itself against the oracle on a sample of rows
+    ref = _ref_gemm(orc, fp8, dict(ops, m_idx=m))
+    got = bits(C)
+    _check_close(got, ref, m >= 0, 5e-3 if not fp8 else 2e-2, fp8)
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("integer_valued", [False, True])
 def test_gemm_masked_all_tile_heights(orc, fp8, integer_valued):
