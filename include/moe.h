@@ -11,7 +11,9 @@
  * General contract
  *   - Every pointer named "device" is a device pointer on the current HIP
  *     device; the caller owns all memory.  The library never allocates: scratch
- *     comes in through ws/ws_bytes (size from moe_scatter_ws_bytes).
+ *     comes in through ws/ws_bytes (size from moe_scatter_ws_bytes); the one
+ *     exception is moe_scatter_compact_noalloc, whose scratch is a static
+ *     device array of fixed size.
  *   - Every compute call validates its arguments on the host first and returns
  *     a status without launching anything when they are wrong; otherwise it
  *     enqueues its kernels on `stream` (a hipStream_t; NULL = default stream)
@@ -151,6 +153,32 @@ int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* 
                             void* x_out, uint8_t* scale_out, int32_t* m_indices,
                             int32_t* expert_start_loc, int32_t* num_valid, int32_t* src2dst,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Largest scratch (bytes, as moe_scatter_ws_bytes counts it) that
+ * moe_scatter_compact_noalloc serves: 4 MiB, e.g. T*k up to about 2^20
+ * assignments with 256 local experts, or 2^18 with 1024. */
+#define MOE_SCATTER_NOALLOC_MAX_BYTES (4u << 20)
+
+/* moe_scatter_compact without the ws/ws_bytes arguments, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, outputs, limits
+ * and status codes as moe_scatter_compact; the scratch is a static device
+ * array of MOE_SCATTER_NOALLOC_MAX_BYTES per device, held until the process
+ * ends.  The call allocates nothing.
+ *   Returns MOE_ECAPACITY when moe_scatter_ws_bytes(T, k, num_local_experts)
+ *   exceeds MOE_SCATTER_NOALLOC_MAX_BYTES, and MOE_EDEVICE when the scratch's
+ *   device address cannot be obtained.
+ * Every call on one device shares that device's scratch: calls that may run
+ * at the same time on one device (different streams without ordering, other
+ * threads) race and give undefined results; calls in one stream are fine.
+ * The compact scatter sets no device error bits, so there is no error word to
+ * read back. */
+int32_t moe_scatter_compact_noalloc(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                                    int32_t k, int32_t expert_start, int32_t num_local_experts,
+                                    int32_t block_e, int64_t rows_capacity, int32_t out_dtype,
+                                    void* x_out, uint8_t* scale_out, int32_t* m_indices,
+                                    int32_t* expert_start_loc, int32_t* num_valid,
+                                    int32_t* src2dst, void* stream);
 
 /* Masked layout, P1 implementation breakdown item 2 (masked branch) and P2 key
  * source excerpt of _BF16GroupedMaskedWarmupExecutor: expert e's rows are

@@ -20,6 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EDEVICE = 0, 1, 2, 3, 4
 MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_UE8M0, MOE_DTYPE_FP8_E4M3_MXFP8, MOE_DTYPE_FP8_MXFP4 = 0, 1, 2, 3
 MOE_MX_E4M3, MOE_MX_E2M1 = 0, 1
 MOE_DEVERR_MASKED_OVERFLOW = 1
+MOE_SCATTER_NOALLOC_MAX_BYTES = 4 << 20
 
 # name -> (restype, argtypes); the exported symbols of include/moe.h
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -33,6 +34,8 @@ SIGNATURES = {
     "moe_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_scatter_compact": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                    _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_scatter_compact_noalloc": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I32,
+                                           _P, _P, _P, _P, _P, _P, _P]),
     "moe_scatter_masked": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                   _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_quant_fp8_ue8m0": (_I32, [_P, _I64, _I32, _I64, _P, _P, _P, _P]),
@@ -159,6 +162,18 @@ def moe_scatter_compact(x, topk_ids, expert_start, num_local_experts, block_e, r
         _ptr(x), T, H, _ptr(topk_ids), k, expert_start, num_local_experts, block_e, rows_capacity,
         _dtype_code(fp8), _ptr(x_out), _ptr(scale_out), _ptr(m_indices), _ptr(expert_start_loc),
         _ptr(num_valid), _ptr(src2dst), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_scatter_compact_noalloc(x, topk_ids, expert_start, num_local_experts, block_e, rows_capacity,
+                                fp8, x_out, scale_out, m_indices, expert_start_loc, num_valid, src2dst):
+    """moe_scatter_compact on the library's static per-device scratch (no ws)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    _check("moe_scatter_compact_noalloc", lib().moe_scatter_compact_noalloc(
+        _ptr(x), T, H, _ptr(topk_ids), k, expert_start, num_local_experts, block_e, rows_capacity,
+        _dtype_code(fp8), _ptr(x_out), _ptr(scale_out), _ptr(m_indices), _ptr(expert_start_loc),
+        _ptr(num_valid), _ptr(src2dst), _stream()))
 
 
 def moe_scatter_masked(x, topk_ids, expert_start, num_local_experts, max_m, fp8, x_out, scale_out,

@@ -13,6 +13,8 @@
 //   4. rows   : one workgroup per token reads its row once and writes it to
 //               each destination row, optionally quantised to e4m3 with
 //               per-128-channel UE8M0 scales.
+#include <mutex>
+
 #include "common.cuh"
 
 namespace moe {
@@ -386,14 +388,18 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
 
 int32_t validate_common(const void* x, int32_t T, int32_t H, const int32_t* ids, int32_t k,
                         int32_t El, int32_t out_dtype, void* x_out, const uint8_t* scale_out,
-                        int32_t* src2dst, void* ws, size_t ws_bytes_given) {
+                        int32_t* src2dst) {
   if (T < 0 || H <= 0 || k < 1 || k > 32 || El < 1 || El > 1024) return MOE_EINVAL;
   if (static_cast<int64_t>(T) * k >= (1ll << 31)) return MOE_EINVAL;
   if (H % 128 != 0) return MOE_EUNSUPPORTED;
   if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3_UE8M0) return MOE_EUNSUPPORTED;
   if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0 && !scale_out) return MOE_EINVAL;
-  if (!ws || ws_bytes_given < ws_bytes(static_cast<int64_t>(T) * k, El)) return MOE_ECAPACITY;
   if (T > 0 && (!x || !ids || !x_out || !src2dst)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int32_t validate_ws(int32_t T, int32_t k, int32_t El, const void* ws, size_t ws_bytes_given) {
+  if (!ws || ws_bytes_given < ws_bytes(static_cast<int64_t>(T) * k, El)) return MOE_ECAPACITY;
   return MOE_OK;
 }
 
@@ -429,18 +435,21 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
                             hipStream_t s) {
   if (A <= kSmallA) {
     const size_t lds = (static_cast<size_t>(kSmallWaves) * El + 1024 + El) * sizeof(int);
-    static bool attr_set[64][2] = {};  // per device, per layout
+    // The LDS limit is raised once per device and layout (thread-safe).
+    static std::once_flag attr_once[64][2];
+    static bool attr_ok[64][2] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
     auto kern = masked ? scatter_front_small_kernel<true> : scatter_front_small_kernel<false>;
-    if (!attr_set[dev][masked ? 1 : 0]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+    const int li = masked ? 1 : 0;
+    std::call_once(attr_once[dev][li], [&]() {
+      attr_ok[dev][li] =
+          hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>((static_cast<size_t>(kSmallWaves) + 1) * 1024 * sizeof(int) +
-                                               1024 * sizeof(int))) != hipSuccess)
-        return MOE_EDEVICE;
-      attr_set[dev][masked ? 1 : 0] = true;
-    }
+                                               1024 * sizeof(int))) == hipSuccess;
+    });
+    if (!attr_ok[dev][li]) return MOE_EDEVICE;
     kern<<<1, 1024, lds, s>>>(ids, static_cast<int>(A), expert_start, El, masked ? 1 : block_e,
                               masked ? max_m : 0, w.start, w.total, start_out, valid_out, src2dst,
                               w.err);
@@ -471,24 +480,18 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
   return MOE_OK;
 }
 
-extern "C" int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
-                                       int32_t k, int32_t expert_start, int32_t El,
-                                       int32_t block_e, int64_t rows_capacity, int32_t out_dtype,
-                                       void* x_out, uint8_t* scale_out, int32_t* m_indices,
-                                       int32_t* expert_start_loc, int32_t* num_valid,
-                                       int32_t* src2dst, void* ws, size_t ws_bytes_given,
-                                       void* stream) {
-  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst, ws,
-                               ws_bytes_given);
-  if (st != MOE_OK) return st;
-  if (block_e <= 0 || block_e % 128 != 0) return MOE_EUNSUPPORTED;
-  if (!expert_start_loc || !num_valid || (rows_capacity > 0 && !m_indices)) return MOE_EINVAL;
+// Everything after argument validation of the compact scatter: the workspace
+// `ws` (at least ws_bytes(T*k, El) bytes) is supplied by the caller or is the
+// library's static scratch array.
+static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                                    int32_t k, int32_t expert_start, int32_t El, int32_t block_e,
+                                    int64_t rows_capacity, int32_t out_dtype, void* x_out,
+                                    uint8_t* scale_out, int32_t* m_indices,
+                                    int32_t* expert_start_loc, int32_t* num_valid,
+                                    int32_t* src2dst, void* ws, hipStream_t s) {
   const int64_t A = static_cast<int64_t>(T) * k;
-  if (rows_capacity < moe_compact_rows_bound(A, El, block_e)) return MOE_ECAPACITY;
-  if (rows_capacity >= (1ll << 31)) return MOE_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const ScatterWs w = carve(ws, A, El);
-  st = launch_front(topk_ids, A, expert_start, El, block_e, w, expert_start_loc, num_valid, false, 0,
+  int32_t st = launch_front(topk_ids, A, expert_start, El, block_e, w, expert_start_loc, num_valid, false, 0,
                     src2dst, s);
   if (st != MOE_OK) return st;
   if (rows_capacity > 0) {
@@ -511,13 +514,92 @@ extern "C" int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, cons
   return MOE_OK;
 }
 
+static int32_t validate_compact(int32_t T, int32_t k, int32_t El, int32_t block_e,
+                                int64_t rows_capacity, const int32_t* m_indices,
+                                const int32_t* expert_start_loc, const int32_t* num_valid) {
+  if (block_e <= 0 || block_e % 128 != 0) return MOE_EUNSUPPORTED;
+  if (!expert_start_loc || !num_valid || (rows_capacity > 0 && !m_indices)) return MOE_EINVAL;
+  if (rows_capacity < moe_compact_rows_bound(static_cast<int64_t>(T) * k, El, block_e))
+    return MOE_ECAPACITY;
+  if (rows_capacity >= (1ll << 31)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                                       int32_t k, int32_t expert_start, int32_t El,
+                                       int32_t block_e, int64_t rows_capacity, int32_t out_dtype,
+                                       void* x_out, uint8_t* scale_out, int32_t* m_indices,
+                                       int32_t* expert_start_loc, int32_t* num_valid,
+                                       int32_t* src2dst, void* ws, size_t ws_bytes_given,
+                                       void* stream) {
+  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst);
+  if (st != MOE_OK) return st;
+  st = validate_ws(T, k, El, ws, ws_bytes_given);
+  if (st != MOE_OK) return st;
+  st = validate_compact(T, k, El, block_e, rows_capacity, m_indices, expert_start_loc, num_valid);
+  if (st != MOE_OK) return st;
+  return scatter_compact_body(x, T, H, topk_ids, k, expert_start, El, block_e, rows_capacity,
+                              out_dtype, x_out, scale_out, m_indices, expert_start_loc, num_valid,
+                              src2dst, ws, static_cast<hipStream_t>(stream));
+}
+
+// Scratch of the allocation-free compact scatter: one copy per device, kept
+// until the process ends.  Host code never passes this name to a kernel or a
+// copy (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_SCATTER_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+static int32_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = p;
+  });
+  if (!g_scratch_ptr[dev]) return MOE_EDEVICE;
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_scatter_compact_noalloc(const void* x, int32_t T, int32_t H,
+                                               const int32_t* topk_ids, int32_t k,
+                                               int32_t expert_start, int32_t El, int32_t block_e,
+                                               int64_t rows_capacity, int32_t out_dtype,
+                                               void* x_out, uint8_t* scale_out,
+                                               int32_t* m_indices, int32_t* expert_start_loc,
+                                               int32_t* num_valid, int32_t* src2dst,
+                                               void* stream) {
+  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst);
+  if (st != MOE_OK) return st;
+  st = validate_compact(T, k, El, block_e, rows_capacity, m_indices, expert_start_loc, num_valid);
+  if (st != MOE_OK) return st;
+  if (ws_bytes(static_cast<int64_t>(T) * k, El) > MOE_SCATTER_NOALLOC_MAX_BYTES) return MOE_ECAPACITY;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  // Nothing in the scratch has to start at zero: the first kernel clears the
+  // error word and every count is written before it is read.
+  return scatter_compact_body(x, T, H, topk_ids, k, expert_start, El, block_e, rows_capacity,
+                              out_dtype, x_out, scale_out, m_indices, expert_start_loc, num_valid,
+                              src2dst, ws, static_cast<hipStream_t>(stream));
+}
+
 extern "C" int32_t moe_scatter_masked(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
                                       int32_t k, int32_t expert_start, int32_t El, int32_t max_m,
                                       int32_t out_dtype, void* x_out, uint8_t* scale_out,
                                       int32_t* masked_m, int32_t* src2dst, void* ws,
                                       size_t ws_bytes_given, void* stream) {
-  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst, ws,
-                               ws_bytes_given);
+  int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst);
+  if (st != MOE_OK) return st;
+  st = validate_ws(T, k, El, ws, ws_bytes_given);
   if (st != MOE_OK) return st;
   if (!masked_m || max_m <= 0) return MOE_EINVAL;
   if (max_m < T) return MOE_ECAPACITY;

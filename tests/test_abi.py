@@ -166,3 +166,25 @@ def test_layer_layout_choice_on_host():
         layer(64, 16, 16, "auto", fp8=False, weight_format="mxfp8")   # MX needs the FP8 path
     with pytest.raises(ValueError):
         layer(64, 16, 16, "auto", fp8=True, weight_format="nvfp4")
+
+
+def test_noalloc_scatter_validates_before_device_work():
+    """moe_scatter_compact_noalloc rejects bad arguments and scratch needs above
+    its static limit on the host, before it looks up its scratch or launches."""
+    lib = L.lib()
+    P = FAKE
+    bound = L.moe_compact_rows_bound(128, 8, 128)
+    args = lambda T, H, k, El, be, R: (P, T, H, P, k, 0, El, be, R, 0, P, P, P, P, P, P, None)
+    assert lib.moe_scatter_compact_noalloc(*args(64, 256, 2, 8, 64, bound)) == L.MOE_EUNSUPPORTED
+    assert lib.moe_scatter_compact_noalloc(*args(64, 200, 2, 8, 128, bound)) == L.MOE_EUNSUPPORTED
+    assert lib.moe_scatter_compact_noalloc(*args(64, 256, 2, 8, 128, bound - 1)) == L.MOE_ECAPACITY
+    assert lib.moe_scatter_compact_noalloc(*args(64, 256, 2, 0, 128, bound)) == L.MOE_EINVAL
+    # 2^23 assignments over 256 experts need more than the 4 MiB static scratch
+    T, k, El = 1 << 20, 8, 256
+    assert L.moe_scatter_ws_bytes(T, k, El) > L.MOE_SCATTER_NOALLOC_MAX_BYTES
+    R = L.moe_compact_rows_bound(T * k, El, 128)
+    assert lib.moe_scatter_compact_noalloc(*args(T, 128, k, El, 128, R)) == L.MOE_ECAPACITY
+    # the limit the header states
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "#define MOE_SCATTER_NOALLOC_MAX_BYTES (4u << 20)" in hdr
+    assert L.MOE_SCATTER_NOALLOC_MAX_BYTES == 4 << 20
