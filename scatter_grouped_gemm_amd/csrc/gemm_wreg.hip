@@ -196,7 +196,19 @@ __device__ __forceinline__ void mfma_drain() {
 }
 
 // M-tiles of a run of nb 128-row blocks
-__device__ __forceinline__ int ntiles_of(int nb) { return (nb * 128 + kMT - 1) / kMT; }
+// The loads of one k-step are spread over the row blocks of the step before
+// (one piece after each block, at most): the texture unit that every vector
+// memory instruction of the CU passes through is the busiest part of the
+// kernel, and a wavefront stalled on it also stops issuing its MFMAs, so
+// bunching the loads into a few blocks left the matrix cores idle there.
+// Entry rb: 1..3 the weights of column block rb (two 16-byte loads), 4 + j
+// activation row group j (j < 8; FP8: 12 the activation scales, 13 the
+// weight scales), -1 nothing.  Column block 0 is loaded in block 0.
+constexpr int kLoadAt[kRB] = {-1, 4, 1, 5, 6, 2, 7, 12, 8, 3, 9, 10, 13, 11, -1, -1};
+
+// M-tiles of a run with z valid rows: as few as the tile height allows, so an
+// expert with at most 256 rows is one tile and its weights stream once
+__device__ __forceinline__ int tiles_of(int z) { return (z + kMT - 1) / kMT; }
 
 // vmcnt <= N, lgkmcnt 0 (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4)
 template <int N>
@@ -295,7 +307,7 @@ __device__ __forceinline__ Tile decode(const int4* table, int nr, int& cur, int 
     r.y = __builtin_amdgcn_readfirstlane(r.y);
     r.z = __builtin_amdgcn_readfirstlane(r.z);
     r.w = __builtin_amdgcn_readfirstlane(r.w);
-    nt = ntiles_of((r.z + 127) >> 7);
+    nt = tiles_of(r.z);
     if (pos < r.x + nt * ntn || cur + 1 >= nr) break;
     ++cur;
   }
@@ -339,6 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   const int nblk = static_cast<int>((p.M + 127) / 128);
   int* const ids = reinterpret_cast<int*>(smem);  // [nblk] first-row ids (stage memory)
   int* const scr = ids + kMaxBlocks + 8;
+  int* const zv = scr + 16;  // [nblk] valid rows of the run ending at block j
+  static_assert((2 * kMaxBlocks + 24) * 4 <= kNS * kActBytes, "set-up arrays fit in the stages");
   for (int j = tid; j < nblk; j += kThreads) {
     const int v = p.m_indices[static_cast<int64_t>(j) * 128];
     ids[j] = (v >= 0 && v < p.G) ? v : -1;
@@ -352,6 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   for (int j = j0; j < j1; ++j)
     if (ids[j] >= 0 && (j == 0 || ids[j - 1] != ids[j])) ls = j;
   const int carry = max(scan_excl_max(ls, scr), -1);
+  // runs ending in this thread's blocks: their valid rows (the last block's
+  // valid rows come first, so a binary search for its first negative entry)
+  // and M-tiles
   int cnt = 0, tsum = 0;
   {
     int S = carry;
@@ -359,8 +376,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       const int v = ids[j];
       if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
       if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
+        const int64_t r0 = static_cast<int64_t>(j) * 128;
+        int lo = 1, hi = p.M - r0 < 128 ? static_cast<int>(p.M - r0) : 128;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (p.m_indices[r0 + mid] >= 0) lo = mid + 1;
+          else hi = mid;
+        }
+        const int z = (j - S) * 128 + lo;
+        zv[j] = z;
         ++cnt;
-        tsum += ntiles_of(j - S + 1);
+        tsum += tiles_of(z);
       }
     }
   }
@@ -379,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       const int v = ids[j];
       if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
       if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
-        const int nt = ntiles_of(j - S + 1);
+        const int nt = tiles_of(zv[j]);
         if ((mb + nt) * ntn <= lo_x) ++c_lo;
         if (mb * ntn < hi_x) ++c_hi;
         mb += nt;
@@ -395,20 +421,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       const int v = ids[j];
       if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
       if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
-        const int nt = ntiles_of(j - S + 1);
+        const int z = zv[j];
+        const int nt = tiles_of(z);
         const int P = mb * ntn, Pe = (mb + nt) * ntn;
-        if (Pe > lo_x && P < hi_x && ri - R0 >= 0 && ri - R0 < kTable) {
-          // valid rows of the run's last block: they come first, so a binary
-          // search for the first negative entry
-          const int64_t r0 = static_cast<int64_t>(j) * 128;
-          int lo = 1, hi = p.M - r0 < 128 ? static_cast<int>(p.M - r0) : 128;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (p.m_indices[r0 + mid] >= 0) lo = mid + 1;
-            else hi = mid;
-          }
-          table[ri - R0] = make_int4(P, S * 128, (j - S) * 128 + lo, v);
-        }
+        if (Pe > lo_x && P < hi_x && ri - R0 >= 0 && ri - R0 < kTable)
+          table[ri - R0] = make_int4(P, S * 128, z, v);
         ++ri;
         mb += nt;
       }
@@ -664,8 +681,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   // blocks earlier; after block 0 one vmcnt wait and one barrier make the next
   // step's stage visible (its loads were issued kLA - 1 steps ago) and free
   // the stage and register set of the step before, which take the loads of the
-  // step kLA ahead, spread over blocks 1 .. 5; the step ends by reading the next
-  // step's first two fragments.
+  // step kLA ahead, spread over blocks 1 .. 13; the step ends by reading the
+  // next step's first two fragments.
   bool c_epi = false, done = false;
   int c_nrb = __builtin_amdgcn_readfirstlane((ct.rows + 15) >> 4);
   const int ck_lo = FP8 ? 2 * fg : fg, ck_hi = FP8 ? 2 * fg + 1 : fg + 4;
@@ -692,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
     read_a(S, 1, 1);
   };
   // The next step's loads were issued kLA - 1 steps ago (the last of them
-  // after block 8); since then kLA - 2 whole steps and this step's first two
+  // after block 13); since then kLA - 2 whole steps and this step's first two
   // weight loads have issued, and vector memory instructions complete in order.
   constexpr int W0 = (kLA - 2) * vm_per_step<FP8>() + 2;
   auto step = [&](auto U) __attribute__((always_inline)) {
@@ -713,17 +730,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
     wait_vm<W0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // blocks 1 .. 11, each followed by its share of the step's loads (weights
-    // first, then the activation rows into the stage freed by the barrier) and
-    // the read of the fragment two blocks on
+    // blocks 1 .. 15, each followed by at most one piece of the step's loads
+    // (kLoadAt) and the read of the fragment two blocks on
 #pragma unroll
     for (int rb = 1; rb < kRB; ++rb) {
       __builtin_amdgcn_sched_barrier(0);
       mma_block<FP8, SILU>(acc[rb], wr[u], af[rb & 1], swa, swb, sa[rb & 1], nrb, rb);
-      if (rb <= 3) issue_w(wr[un], rb);
-      if (rb >= 4 && rb <= 8) {
-        issue_a(un, 2 * (rb - 4));
-        issue_a(un, 2 * (rb - 4) + 1);
+      {
+        const int it = kLoadAt[rb];
+        if (it >= 1 && it <= 3) issue_w(wr[un], it);
+        else if (it >= 4 && it - 4 < kALD + (FP8 ? 2 : 0)) issue_a(un, it - 4);
       }
       if (rb + 2 < kRB) read_a(S, rb + 2, rb & 1);
     }
