@@ -22,6 +22,8 @@ import time
 METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (BF16/FP8) as % of MFMA peak, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0
+# the other seeded workloads, timed after the headline one in the same run
+OTHER_WORKLOADS = ("tiny", "bf16_prefill", "fp8_decode", "bf16_skewed")
 
 
 def log(*a):
@@ -47,6 +49,10 @@ def parse():
                     help="skip the dense vendor-library GEMMs timed for reference")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--workloads", default=",".join(OTHER_WORKLOADS),
+                    help="comma-separated further workloads timed in the same run and reported "
+                         "under 'workloads' ('' for none)")
+    ap.add_argument("--workload-steps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -95,11 +101,16 @@ def gemm_work(wl, layer, torch):
     w13_out = (I * (ab + asc)) if layer.fuse_silu else (2 * I * 2)
     w13_bytes = active * 2 * I * H * (wb + sc) + A * H * (ab + asc) + A * w13_out
     w2_bytes = active * H * I * (wb + sc) + A * I * (ab + asc) + A * H * 2
-    # rows of the tiles the GEMMs execute (whole tiles, padding included)
-    bm = 64 if layer.layout == "masked" and 0 < layer.expected_m <= 64 else 128
-    rows_exec = int(((counts + bm - 1) // bm * bm).sum())
+    # rows on which the GEMMs run their MFMAs (whole 16-row blocks of their
+    # tiles, padding included), from the library's own tile rule
+    from scatter_grouped_gemm_amd import _lib as L
+    masked = layer.layout == "masked"
+    M = layer.rows if not masked else layer.max_m
+    c = counts.numpy()
+    rows13 = L.grouped_gemm_rows_executed(layer.wdt, masked, c, layer.expected_m, M, 2 * I, H)
+    rows2 = L.grouped_gemm_rows_executed(layer.wdt, masked, c, layer.expected_m, M, H, I)
     return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
-                exec_flops=2.0 * rows_exec * (2 * I * H + H * I),
+                exec_flops=2.0 * (rows13 * 2 * I * H + rows2 * H * I),
                 w13_bytes=w13_bytes, w2_bytes=w2_bytes)
 
 
@@ -119,23 +130,33 @@ def roofline(flops, nbytes, ms, dtype):
                 arithmetic_intensity=round(ai, 1))
 
 
+# the sources the grouped-GEMM kernels are built from: counter figures taken
+# on other sources are not reported
+GEMM_SOURCES = ("gemm.hip", "gemm_wreg.hip", "gemm_wreg.h", "common.h")
+
+
+def gemm_source_sha256():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for src in GEMM_SOURCES:
+        with open(os.path.join(root, "scatter_grouped_gemm_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(wl_name, which):
     """HBM bytes per launch of one grouped GEMM (FETCH_SIZE + WRITE_SIZE, scaled
     by a plain copy's reading) from the rocprofv3 counter summary committed
     under profiles/, or None when there is none for this workload or the GEMM
     source has changed since the counters were taken."""
-    import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"traffic_{wl_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    h = hashlib.sha256()
-    for src in ("gemm.hip", "common.cuh"):
-        with open(os.path.join(root, "scatter_grouped_gemm_amd", "csrc", src), "rb") as f:
-            h.update(f.read())
-    if d.get("gemm_source_sha256") != h.hexdigest() or which not in d:
+    if d.get("gemm_source_sha256") != gemm_source_sha256() or which not in d:
         return None
     return int(d[which]["read_bytes"] + d[which]["write_bytes"])
 
@@ -211,6 +232,44 @@ def graph_steps(layer, x, logits, steps, torch):
     torch.cuda.synchronize()
     del graph
     return start.elapsed_time(end) / steps
+
+
+def workload_summary(wl, layer, ms, kern, torch):
+    """tokens/s, per-kernel times and both GEMMs' rooflines of one timed run."""
+    work = gemm_work(wl, layer, torch)
+    dtype = "fp8_e4m3" if wl.fp8 else "bf16"
+    w13_key = "gemm_w13_silu" if layer.fuse_silu else "gemm_w13"
+    out = {"workload": wl.name, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+           "ms_per_step": round(ms, 4), "dtype": dtype, "layout": layer.layout,
+           "assignments": work["assignments"], "kernels_ms": {k: round(v, 4) for k, v in kern.items()}}
+    for name, key, flops, nbytes in (("w13", w13_key, work["w13_flops"], work["w13_bytes"]),
+                                     ("w2", "gemm_w2", work["w2_flops"], work["w2_bytes"])):
+        r = roofline(flops, nbytes, kern[key], dtype)
+        r["traffic"] = measured_traffic(wl.name, name)
+        r["ms"] = round(kern[key], 4)
+        out[f"{name}_roofline"] = r
+    gemm_ms = kern[w13_key] + kern["gemm_w2"]
+    tf = (work["w13_flops"] + work["w2_flops"]) / (gemm_ms * 1e-3) / 1e12
+    out["gemm"] = {"tflops_both": round(tf, 1), "mfma_frac_both": round(tf / PEAK_TFLOPS[dtype], 4),
+                   "executed_tflops_both": round(work["exec_flops"] / (gemm_ms * 1e-3) / 1e12, 1)}
+    out["memory_kernels"] = memory_kernels(wl, layer, kern, work)
+    return out
+
+
+def other_workloads(names, torch, steps, warmup=3):
+    """The further seeded workloads, each built, timed and freed in turn."""
+    from scatter_grouped_gemm_amd import inputs
+    out = {}
+    for name in names:
+        wl = inputs.get(name)
+        log(f"workload {wl.name}")
+        layer, x, logits = build_layer(wl, torch)
+        ms, kern = time_steps(layer, x, logits, steps, warmup, torch)
+        log(f"{name}: {ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+        out[name] = workload_summary(wl, layer, ms, kern, torch)
+        del layer, x, logits
+        torch.cuda.empty_cache()
+    return out
 
 
 def mx_variants(wl, x, logits, torch, steps=10, warmup=3):
@@ -447,6 +506,11 @@ def main():
             if isinstance(v, dict)))
     if not args.no_cpu_baseline and not layer.mx:
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
+    names = [n for n in args.workloads.split(",") if n and n != args.workload]
+    if names:
+        del layer, x, logits
+        torch.cuda.empty_cache()
+        res["workloads"] = other_workloads(names, torch, args.workload_steps)
     print(json.dumps(res), flush=True)
 
 

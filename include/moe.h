@@ -101,7 +101,10 @@ const char* moe_status_str(int32_t status);
 
 /* Copies the device error word kept at the start of a scatter workspace to
  * *host_err after waiting for `stream`; 0 means no data-dependent error was
- * seen by the last scatter call that used this workspace.  Synchronises. */
+ * seen by the last scatter call that used this workspace.  Synchronises: this
+ * is the one call that blocks the host (it waits for `stream` itself), unlike
+ * the enqueue-only contract of every other call, where synchronising is left
+ * to the caller. */
 int32_t moe_get_device_error(const void* ws, int32_t* host_err, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -262,6 +265,16 @@ int32_t moe_mx_scales_tile(const uint8_t* scale_plain, int32_t G, int32_t N, int
  * Limits: N % 128 == 0, K % 128 == 0. */
 int32_t moe_requant_weight_fp8_ue8m0(const uint8_t* q_in, const float* s_in, int32_t G, int32_t N,
                                      int32_t K, uint8_t* q_out, uint8_t* s_out, void* stream);
+
+/* Rows on which a grouped GEMM call runs its MFMAs (whole 16-row blocks of
+ * its tiles, padding included), for throughput accounting: the tile choice of
+ * grouped_gemm_masked(_silu) with this expected_m (masked != 0), or of
+ * grouped_gemm_contig(_silu) on a layout with M rows in which each of the G
+ * experts is one run of counts[g] valid rows (what moe_scatter_compact
+ * writes).  counts: host int32 [G].  N is the GEMM's output width (2I for
+ * the SiLU variants).  Returns -1 on a null pointer or negative size. */
+int64_t grouped_gemm_rows_executed(int32_t dtype, int32_t masked, const int32_t* counts, int32_t G,
+                                   int32_t expected_m, int64_t M, int32_t N, int32_t K);
 
 /* ---------------------------------------------------------------------------
  * Grouped GEMMs ("NT": C = A . B[g]^T), fp32 accumulation, bf16 output

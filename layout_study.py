@@ -9,7 +9,7 @@ one up to a crossover in token count ("Support DeepGEMM for standard MoE
 dispatch", comments section).  This sweep measures where that crossover lies
 for these kernels.
 
-    python -m scatter_grouped_gemm_amd.layout_study [--shapes fp8_e256,fp8_e32,bf16_e128]
+    python layout_study.py [--shapes fp8_e256,fp8_e32,bf16_e128]
         [--tokens 16,64,...] [--steps 10] [--warmup 3] [--md out.md]
 
 The masked layout holds max_m = T rows per local expert, so its buffers grow
@@ -26,7 +26,7 @@ import time
 
 import torch
 
-from . import MoELayer, inputs
+from scatter_grouped_gemm_amd import MoELayer, inputs
 
 # (name, H, I, E, E_local, k, fp8, workload whose weight seeds are used)
 SHAPES = {

@@ -43,6 +43,7 @@ SIGNATURES = {
     "moe_requant_weight_fp8_ue8m0": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "moe_quant_weight_mx": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "moe_mx_scales_tile": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
+    "grouped_gemm_rows_executed": (_I64, [_I32, _I32, _P, _I32, _I32, _I64, _I32, _I32]),
     "grouped_gemm_contig": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "grouped_gemm_masked": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "grouped_gemm_contig_silu": (_I32, [_I32, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _I32,
@@ -140,6 +141,18 @@ def moe_get_device_error(ws: torch.Tensor) -> int:
     _check("moe_get_device_error", lib().moe_get_device_error(_ptr(ws), ctypes.byref(out), _stream()))
     return int(out.value)
 
+
+
+def grouped_gemm_rows_executed(fp8, masked: bool, counts, expected_m: int, M: int, N: int, K: int) -> int:
+    """Rows the grouped GEMM with these arguments runs its MFMAs on (whole
+    16-row blocks of its tiles) for per-expert valid counts."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(counts, np.int32))
+    r = lib().grouped_gemm_rows_executed(_gemm_dtype(fp8), int(bool(masked)),
+                                         c.ctypes.data_as(ctypes.c_void_p), len(c), expected_m, M, N, K)
+    if r < 0:
+        raise ValueError("grouped_gemm_rows_executed: bad arguments")
+    return int(r)
 
 
 # --- device calls ----------------------------------------------------------------

@@ -5,7 +5,7 @@
 // summed in order j = 0..k-1 with explicit round-to-nearest fp32 multiply and
 // add (no contraction), so the result is the same for a token whatever batch
 // it arrives in.
-#include "common.cuh"
+#include "common.h"
 
 namespace moe {
 

@@ -53,7 +53,7 @@
 #include <mutex>
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 #include "gemm_wreg.h"
 
 namespace moe {
@@ -1067,6 +1067,50 @@ extern "C" int32_t grouped_gemm_contig(int32_t dtype, const void* A, const uint8
   return launch_dtype<128, 128, false>(dtype, a, s);
 }
 
+// Rows of tile height bm the masked kernels use for this hint (the rule the
+// launches below apply; SiLU always has N = 2I % 256 == 0).
+static int masked_tile_rows(int32_t expected_m, int32_t N) {
+  if (expected_m > 0 && expected_m <= 16 && N % 256 == 0) return 16;
+  if (expected_m > 0 && expected_m <= 32 && N % 256 == 0) return 32;
+  if (expected_m > 0 && expected_m <= 64) return 64;
+  return 128;
+}
+
+extern "C" int64_t grouped_gemm_rows_executed(int32_t dtype, int32_t masked, const int32_t* counts,
+                                              int32_t G, int32_t expected_m, int64_t M, int32_t N,
+                                              int32_t K) {
+  if (!counts || G <= 0 || N <= 0 || K <= 0 || M < 0 || expected_m < 0) return -1;
+  int64_t rows = 0;
+  if (masked) {
+    const int64_t bm = masked_tile_rows(expected_m, N);
+    for (int g = 0; g < G; ++g) {
+      if (counts[g] < 0) return -1;
+      rows += (counts[g] + bm - 1) / bm * bm;
+    }
+    return rows;
+  }
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  const bool wreg = (fp8 || dtype == MOE_DTYPE_BF16) && wreg_supported(M, N, K, G, fp8);
+  for (int g = 0; g < G; ++g) {
+    const int64_t z = counts[g];
+    if (z < 0) return -1;
+    if (z == 0) continue;
+    if (!wreg) {
+      rows += (z + 127) / 128 * 128;
+      continue;
+    }
+    // the register-streamed kernel: ceil(z / 256) tiles of equal height
+    // rounded up to 16, each running its MFMAs on whole 16-row blocks
+    const int64_t nt = (z + 255) / 256;
+    const int64_t h = ((z + nt - 1) / nt + 15) / 16 * 16;
+    for (int64_t t = 0; t < nt; ++t) {
+      const int64_t r = z - t * h < h ? z - t * h : h;
+      if (r > 0) rows += (r + 15) / 16 * 16;
+    }
+  }
+  return rows;
+}
+
 extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8_t* A_scale,
                                        const void* B, const uint8_t* B_scale, void* C,
                                        const int32_t* masked_m, int32_t expected_m, int32_t max_m,
@@ -1090,14 +1134,12 @@ extern "C" int32_t grouped_gemm_masked(int32_t dtype, const void* A, const uint8
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool n256 = N % 256 == 0;
   // tile height from the hint: small expected counts waste less work on 64 rows
-  if (expected_m > 0 && expected_m <= 16 && N % 256 == 0) return launch_dtype<16, 256, true>(dtype, a, s);
-  if (expected_m > 0 && expected_m <= 32 && N % 256 == 0) return launch_dtype<32, 256, true>(dtype, a, s);
-  if (expected_m > 0 && expected_m <= 64) {
-    if (n256) return launch_dtype<64, 256, true>(dtype, a, s);
-    return launch_dtype<64, 128, true>(dtype, a, s);
+  switch (masked_tile_rows(expected_m, N)) {
+    case 16: return launch_dtype<16, 256, true>(dtype, a, s);
+    case 32: return launch_dtype<32, 256, true>(dtype, a, s);
+    case 64: return n256 ? launch_dtype<64, 256, true>(dtype, a, s) : launch_dtype<64, 128, true>(dtype, a, s);
+    default: return n256 ? launch_dtype<128, 256, true>(dtype, a, s) : launch_dtype<128, 128, true>(dtype, a, s);
   }
-  if (n256) return launch_dtype<128, 256, true>(dtype, a, s);
-  return launch_dtype<128, 128, true>(dtype, a, s);
 }
 
 // The w13 GEMM with SiLU-and-mul in its epilogue: B holds [G][2I][K] (gate
@@ -1175,18 +1217,14 @@ extern "C" int32_t grouped_gemm_masked_silu(int32_t dtype, const void* A, const 
   a.G = G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool q8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
-  if (expected_m > 0 && expected_m <= 16) {
-    if (q8) return launch_dtype<16, 256, true, kEpiSiluFp8>(dtype, a, s);
-    return launch_dtype<16, 256, true, kEpiSiluBf16>(dtype, a, s);
+  switch (masked_tile_rows(expected_m, 2 * I)) {
+    case 16: return q8 ? launch_dtype<16, 256, true, kEpiSiluFp8>(dtype, a, s)
+                       : launch_dtype<16, 256, true, kEpiSiluBf16>(dtype, a, s);
+    case 32: return q8 ? launch_dtype<32, 256, true, kEpiSiluFp8>(dtype, a, s)
+                       : launch_dtype<32, 256, true, kEpiSiluBf16>(dtype, a, s);
+    case 64: return q8 ? launch_dtype<64, 256, true, kEpiSiluFp8>(dtype, a, s)
+                       : launch_dtype<64, 256, true, kEpiSiluBf16>(dtype, a, s);
+    default: return q8 ? launch_dtype<128, 256, true, kEpiSiluFp8>(dtype, a, s)
+                       : launch_dtype<128, 256, true, kEpiSiluBf16>(dtype, a, s);
   }
-  if (expected_m > 0 && expected_m <= 32) {
-    if (q8) return launch_dtype<32, 256, true, kEpiSiluFp8>(dtype, a, s);
-    return launch_dtype<32, 256, true, kEpiSiluBf16>(dtype, a, s);
-  }
-  if (expected_m > 0 && expected_m <= 64) {
-    if (q8) return launch_dtype<64, 256, true, kEpiSiluFp8>(dtype, a, s);
-    return launch_dtype<64, 256, true, kEpiSiluBf16>(dtype, a, s);
-  }
-  if (q8) return launch_dtype<128, 256, true, kEpiSiluFp8>(dtype, a, s);
-  return launch_dtype<128, 256, true, kEpiSiluBf16>(dtype, a, s);
 }

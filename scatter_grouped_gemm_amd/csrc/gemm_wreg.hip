@@ -55,7 +55,7 @@
 #include <mutex>
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 #include "gemm_wreg.h"
 
 namespace moe {

@@ -4,7 +4,7 @@
 // Row kernels use one wavefront per row: each lane owns 8 consecutive
 // channels (16 bytes of bf16), so 16 lanes hold one 128-channel group and the
 // group maximum is a 4-step butterfly inside those 16 lanes.
-#include "common.cuh"
+#include "common.h"
 
 namespace moe {
 

@@ -4,7 +4,7 @@
 // probable experts are the k largest logits); equal logits go to the lower
 // expert index.  Weights are the chosen softmax terms renormalised over the k:
 // w_j = exp(L_j - L_max) / sum_i exp(L_i - L_max), in fp32, summed in slot order.
-#include "common.cuh"
+#include "common.h"
 
 namespace moe {
 

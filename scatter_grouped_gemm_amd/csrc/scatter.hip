@@ -15,7 +15,7 @@
 //               per-128-channel UE8M0 scales.
 #include <mutex>
 
-#include "common.cuh"
+#include "common.h"
 
 namespace moe {
 

@@ -7,6 +7,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from scatter_grouped_gemm_amd import _lib as L
@@ -188,3 +189,52 @@ def test_noalloc_scatter_validates_before_device_work():
     hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
     assert "#define MOE_SCATTER_NOALLOC_MAX_BYTES (4u << 20)" in hdr
     assert L.MOE_SCATTER_NOALLOC_MAX_BYTES == 4 << 20
+
+
+def _rows_exec_reference(masked, counts, expected_m, N, wreg):
+    """The tile rules written out: masked tiles of 16/32/64/128 rows chosen by
+    the hint (16 and 32 only when N % 256 == 0); compact, the register-streamed
+    kernel's ceil(z/256) equal tiles rounded up to 16 rows, each running whole
+    16-row blocks, else 128-row tiles."""
+    total = 0
+    for z in counts:
+        if masked:
+            if 0 < expected_m <= 16 and N % 256 == 0:
+                bm = 16
+            elif 0 < expected_m <= 32 and N % 256 == 0:
+                bm = 32
+            elif 0 < expected_m <= 64:
+                bm = 64
+            else:
+                bm = 128
+            total += -(-z // bm) * bm
+        elif z > 0 and wreg:
+            nt = -(-z // 256)
+            h = -(-(-(-z // nt)) // 16) * 16
+            for t in range(nt):
+                r = min(h, z - t * h)
+                if r > 0:
+                    total += -(-r // 16) * 16
+        elif z > 0:
+            total += -(-z // 128) * 128
+    return total
+
+
+def test_grouped_gemm_rows_executed_follows_the_tile_rules():
+    rng = np.random.default_rng(3)
+    for counts in ([0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 4097],
+                   rng.integers(0, 700, 50).tolist()):
+        M = sum(-(-c // 128) * 128 for c in counts) + 128
+        for em in (0, 8, 16, 24, 32, 50, 64, 65):
+            for N in (256, 384, 4096):
+                assert L.grouped_gemm_rows_executed(True, True, counts, em, M, N, 512) == \
+                    _rows_exec_reference(True, counts, em, N, False), (em, N)
+        for fp8 in (False, True, "mxfp8"):
+            for N in (256, 384, 4096):
+                wreg = fp8 in (False, True) and N % 256 == 0
+                assert L.grouped_gemm_rows_executed(fp8, False, counts, 0, M, N, 512) == \
+                    _rows_exec_reference(False, counts, 0, N, wreg), (fp8, N)
+    # one expert of 257 rows: two tiles of 144 and 113 rows -> 144 + 128
+    assert L.grouped_gemm_rows_executed(True, False, [257], 0, 384, 4096, 7168) == 272
+    with pytest.raises(ValueError):
+        L.grouped_gemm_rows_executed(True, False, [-1], 0, 128, 256, 256)
