@@ -344,11 +344,20 @@ def test_gemm_mx_contig(orc, counts, N, K, integer_valued, fmt):
         _check_close(got, ref, valid, 2e-2, True)
 
 
+def _masked_tile_rows(fp8, expected_m, N, K, max_m):
+    """The masked kernels' tile height for this hint, from the library (one
+    valid row executes one whole tile)."""
+    return L.grouped_gemm_rows_executed(fp8, True, [1], expected_m, max_m, N, K)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-@pytest.mark.parametrize("expected_m", [0, 8])
+@pytest.mark.parametrize("expected_m", [0, 8, 24, 50])
 def test_gemm_mx_masked(orc, expected_m, fmt):
+    """MX weights, masked layout, every tile height (128, 16, 32, 64 rows),
+    two N-tiles: bit-exact against the oracle, rows past each group's last
+    tile untouched."""
     announce("gemm_mx_masked", fmt, expected_m)
-    G, max_m, N, K = 5, 200, 256, 384
+    G, max_m, N, K = 5, 200, 512, 384
     masked = np.array([0, 1, 200, 37, 130], np.int32)
     ops = _mx_operands(orc, [max_m] * G, N, K, seed=31, integer_valued=True, fmt=fmt)
     rg = orc.masked_row_group(masked, max_m)
@@ -363,6 +372,9 @@ def test_gemm_mx_masked(orc, expected_m, fmt):
     got = bits(C).reshape(G * max_m, N)
     valid = rg >= 0
     assert np.array_equal(got[valid], ref[valid])
+    bm = _masked_tile_rows(fmt, expected_m, N, K, max_m)
+    assert bm == {0: 128, 8: 16, 24: 32, 50: 64}[expected_m]
+    assert np.all(got[_skipped_rows_masked(masked, max_m, bm)] == 0xFFFF)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
@@ -397,7 +409,8 @@ def test_gemm_mx_silu_fused_matches_separate(orc, out_fp8, fmt):
 # grouped GEMMs
 # ---------------------------------------------------------------------------
 
-def _gemm_operands(orc, fp8, M_counts, N, K, seed, integer_valued=False, block_e=128, extra_rows=128):
+def _gemm_operands(orc, fp8, M_counts, N, K, seed, integer_valued=False, block_e=128, extra_rows=128,
+                   scale_ranges=((125, 130), (124, 129))):
     G = len(M_counts)
     m_idx = compact_layout(M_counts, block_e, extra_rows)
     M = len(m_idx)
@@ -415,8 +428,9 @@ def _gemm_operands(orc, fp8, M_counts, N, K, seed, integer_valued=False, block_e
         qa = A.float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         qb = B.float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         rng = np.random.default_rng(seed)
-        sa = rng.integers(125, 130, (M, K // 128)).astype(np.uint8)
-        sb = rng.integers(124, 129, (G, N // 128, K // 128)).astype(np.uint8)
+        (a0, a1), (b0, b1) = scale_ranges
+        sa = rng.integers(a0, a1, (M, K // 128)).astype(np.uint8)
+        sb = rng.integers(b0, b1, (G, N // 128, K // 128)).astype(np.uint8)
         return dict(m_idx=m_idx, A=qa, As=sa, B=qb, Bs=sb)
     qa, sa = orc.quant_rows(bits(A))
     qb, sb = orc.quant_weight_blocks(bits(B))
@@ -649,6 +663,26 @@ def test_gemm_silu_fused_many_tiles_per_workgroup(orc, fp8, out_fp8):
     _check_close(got, ref, m >= 0, 5e-3 if not fp8 else 2e-2, fp8)
 
 
+@pytest.mark.parametrize("fp8,counts,N,K", [
+    (True, [257, 5, 0, 130], 4096, 7168),     # FP8 w13 of the DeepSeek-V3-shaped prefill
+    (False, [130, 3], 28672, 4096),           # BF16 w13 of the Mixtral-shaped prefill
+])
+def test_gemm_contig_integer_exact_real_shapes(orc, fp8, counts, N, K):
+    """The compact GEMM at the workloads' real N and K (many N-tiles, 56 or 64
+    k-steps, an expert split into two M-tiles, a one-row-block tile) with
+    integer-valued operands: every partial sum is exact in fp32 (BF16:
+    |sum| <= 12 K < 2^24; FP8: scale exponents within [-2, 1], so block sums
+    of at most 1536 stay within 20 bits), so the result must be bit-exact."""
+    announce("gemm_contig_real_shape", fp8, counts, N, K)
+    ops = _gemm_operands(orc, fp8, counts, N, K, seed=61, integer_valued=True,
+                         scale_ranges=((126, 129), (126, 128)))
+    ref = _ref_gemm(orc, fp8, ops)
+    got = _run_contig(fp8, ops, N)
+    valid = ops["m_idx"] >= 0
+    assert np.array_equal(got[valid], ref[valid])
+    assert np.all(got[_skipped_rows_contig(ops["m_idx"])] == 0xFFFF)
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("integer_valued", [False, True])
 def test_gemm_masked_all_tile_heights(orc, fp8, integer_valued):
@@ -788,11 +822,13 @@ def test_gemm_silu_fused_contig(orc, fp8, out_fp8):
 
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("out_fp8", [False, True])
-@pytest.mark.parametrize("expected_m", [0, 8])
+@pytest.mark.parametrize("expected_m", [0, 8, 24, 50])
 def test_gemm_silu_fused_masked(orc, fp8, out_fp8, expected_m):
-    """Masked layout, both tile heights: fused equals separate bit for bit."""
+    """Masked layout, every tile height (128, 16, 32, 64 rows) and four
+    N-tiles: fused equals separate bit for bit; rows past each group's last
+    tile are untouched."""
     announce("gemm_silu_masked", fp8, out_fp8, expected_m)
-    G, max_m, I, K = 5, 200, 256, 256
+    G, max_m, I, K = 5, 200, 512, 256
     masked = np.array([0, 1, 200, 37, 130], np.int32)
     ops = _gemm_operands(orc, fp8, [max_m] * G, 2 * I, K, seed=23)
     A = ops["A"][: G * max_m]
@@ -822,6 +858,12 @@ def test_gemm_silu_fused_masked(orc, fp8, out_fp8, expected_m):
         fs, ss = fused_s.cpu().numpy(), sep_s.cpu().numpy()
         for g in range(G):
             assert np.array_equal(fs[g, :, : masked[g]], ss[g, :, : masked[g]])
+    bm = _masked_tile_rows(fp8, expected_m, 2 * I, K, max_m)
+    assert bm == {0: 128, 8: 16, 24: 32, 50: 64}[expected_m]
+    skipped = torch.from_numpy(_skipped_rows_masked(masked, max_m, bm))
+    untouched = 0xFF if out_fp8 else -1
+    raw = fused.cpu().view(G * max_m, I).view(torch.uint8 if out_fp8 else torch.int16)
+    assert bool((raw[skipped] == untouched).all())
 
 
 # ---------------------------------------------------------------------------

@@ -3,20 +3,23 @@ bench.py times (the same MoELayer construction).
 
 At full size the oracle cannot run the whole batch in seconds, so: routing and
 every layout index are compared bit-exactly for ALL tokens; a sample of
-scattered rows is compared bit-exactly; the outputs of a sample of tokens are
-compared with the oracle's layout-free per-token path (valid because each
-token's output depends only on its own row, which the batch-invariance checks
-confirm on the GPU)."""
+scattered rows is compared bit-exactly; the outputs of 256 tokens (all of them
+when the batch is smaller) are compared element by element with the oracle's
+layout-free per-token path (valid because each token's output depends only on
+its own row, which the batch-invariance checks confirm on the GPU).  The
+sample always holds tokens routed to the hottest and to the coldest live
+expert and tokens whose rows are the last rows of an expert (the last,
+partial M-tile of its run), the rest drawn at random."""
 import numpy as np
 import pytest
 import torch
 
 from scatter_grouped_gemm_amd import MoELayer, inputs
-from gpu_util import DEV, announce, bits, f32, rel_fro
+from gpu_util import DEV, announce, bf16_ulp, bits, f32, rel_fro
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny": 64, "bf16_prefill": 8, "fp8_prefill": 6, "fp8_decode": 256, "bf16_skewed": 12}
+N_SAMPLE = 256
 
 
 def _build(wl):
@@ -28,6 +31,48 @@ def _build(wl):
         a, b = inputs.expert_weights(wl, wl.expert_start + e, DEV)
         layer.set_expert(e, a, b)
     return layer
+
+
+# Element-wise slack (fraction of the row's largest output) beyond one bf16
+# ulp.  The GPU and the oracle sum in different orders, so an intermediate
+# bf16 (the w13 output, the SiLU product) can land one ulp apart; FP8 then
+# requantises the activation to e4m3, where such a difference occasionally
+# moves a code by one e4m3 step (up to 1/8 of that element), and the w2 sum
+# carries it into every output of the token.  Measured worst cases over the
+# 256-token samples on MI355X: 3.8e-3 (BF16 workloads) and 6.4e-3 (FP8); the
+# bounds leave about a factor three.  The relative-Frobenius bounds are the
+# method's stated tolerances (5e-3 BF16, 2e-2 FP8).
+ELEMENT_SLACK = {False: 1e-2, True: 2e-2}
+
+
+def _pick_tokens(wl, s2d, counts, rng):
+    """N_SAMPLE tokens: those routed to the hottest and to the coldest live
+    expert (up to 16 each), those holding the last 4 rows of up to 16 live
+    experts, then random ones."""
+    T = s2d.shape[0]
+    if T <= N_SAMPLE:
+        return np.arange(T)
+    # assignments in destination-row order: both layouts keep an expert's rows
+    # contiguous, experts in increasing order, so the sorted sequence is
+    # counts[0] rows of expert 0, then counts[1] of expert 1, ...
+    flat = s2d.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    order = order[flat[order] >= 0]
+    tok_sorted = order // s2d.shape[1]
+    exp_of = np.repeat(np.arange(len(counts)), counts)
+    assert len(exp_of) == len(tok_sorted)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    live = np.nonzero(counts > 0)[0]
+    hot, cold = live[np.argmax(counts[live])], live[np.argmin(counts[live])]
+    pick = []
+    for e in (hot, cold):
+        pick += list(tok_sorted[exp_of == e][:16])
+    for e in rng.choice(live, size=min(16, len(live)), replace=False):
+        pick += list(tok_sorted[starts[e + 1] - min(4, counts[e]):starts[e + 1]])
+    pick = list(dict.fromkeys(int(t) for t in pick))[:N_SAMPLE]
+    rest = np.setdiff1d(np.arange(T), pick)
+    pick += [int(t) for t in rng.choice(rest, size=N_SAMPLE - len(pick), replace=False)]
+    return np.sort(np.array(pick, np.int64))
 
 
 def _oracle_tokens(orc, wl, xs_bits, ids, w):
@@ -101,13 +146,19 @@ def test_workload_full_size(orc, name):
         xg = bits(layer.x_buf[torch.from_numpy(rows).long().to(DEV)])
         assert np.array_equal(xg, xb[ts[pick]])
     # sampled token outputs against the oracle's per-token path
-    n = min(SAMPLE[name], T)
-    tok = np.sort(rng.choice(T, size=n, replace=False))
-    ref = _oracle_tokens(orc, wl, xb[tok], ids_ref[tok], w_ref[tok])
+    tok = _pick_tokens(wl, s2d, counts, rng)
+    ref = f32(_oracle_tokens(orc, wl, xb[tok], ids_ref[tok], w_ref[tok])).astype(np.float64)
     got = f32(bits(out)[tok]).astype(np.float64)
     assert np.all(np.isfinite(got))
-    err = rel_fro(got, f32(ref))
+    err = rel_fro(got, ref)
+    # element-wise: one bf16 ulp of the reference element plus a slack scaled
+    # by the row's largest element (see ELEMENT_SLACK)
+    excess = np.abs(got - ref) - bf16_ulp(ref)
+    worst = float(np.max(excess / np.abs(ref).max(axis=1, keepdims=True)))
+    print(f"[parity] {wl.name}: {len(tok)} tokens, rel-Frobenius {err:.3e}, "
+          f"worst element excess over 1 ulp / row max {worst:.3e}", flush=True)
     assert err <= (2e-2 if wl.fp8 else 5e-3), err
+    assert worst <= ELEMENT_SLACK[wl.fp8], worst
     # batch invariance at the workload's own shape (the skewed workload is
     # specified with T = 1, 7, 33 as well)
     full = bits(out).copy()
