@@ -93,8 +93,10 @@ int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_experts);
 int32_t moe_choose_layout(int64_t max_tokens, int32_t num_local_experts);
 
 /* Scratch bytes moe_scatter_compact / moe_scatter_masked need for T tokens,
- * top-k and num_local_experts local experts. */
-size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts);
+ * top-k, num_local_experts local experts and H hidden channels (per-chunk
+ * expert counts, per-expert starts and totals, the assignment of each valid
+ * row, and FP8 scale bytes staged per token).  0 on a negative size. */
+size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts, int32_t H);
 
 /* Static text for a status code. */
 const char* moe_status_str(int32_t status);
@@ -146,7 +148,7 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  *   expert_start_loc  device int32 [num_local_experts], out: first row of e
  *   num_valid         device int32 [num_local_experts], out: rows of e
  *   src2dst           device int32 [T][k], out: row of (t, j), -1 if not local
- *   ws, ws_bytes      scratch, at least moe_scatter_ws_bytes(T, k, El)
+ *   ws, ws_bytes      scratch, at least moe_scatter_ws_bytes(T, k, El, H)
  * Limits: H % 128 == 0, block_e a positive multiple of 128 (the grouped GEMM
  * tiles never straddle experts), 1 <= num_local_experts <= 1024,
  * rows_capacity < 2^31. */
@@ -158,8 +160,8 @@ int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* 
                             void* ws, size_t ws_bytes, void* stream);
 
 /* Largest scratch (bytes, as moe_scatter_ws_bytes counts it) that
- * moe_scatter_compact_noalloc serves: 4 MiB, e.g. T*k up to about 2^20
- * assignments with 256 local experts, or 2^18 with 1024. */
+ * moe_scatter_compact_noalloc serves: 4 MiB, e.g. T = 32768 tokens, top-8,
+ * H = 7168 with 256 local experts (about 3.75 MiB). */
 #define MOE_SCATTER_NOALLOC_MAX_BYTES (4u << 20)
 
 /* moe_scatter_compact without the ws/ws_bytes arguments, for callers that
@@ -168,7 +170,7 @@ int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, const int32_t* 
  * and status codes as moe_scatter_compact; the scratch is a static device
  * array of MOE_SCATTER_NOALLOC_MAX_BYTES per device, held until the process
  * ends.  The call allocates nothing.
- *   Returns MOE_ECAPACITY when moe_scatter_ws_bytes(T, k, num_local_experts)
+ *   Returns MOE_ECAPACITY when moe_scatter_ws_bytes(T, k, num_local_experts, H)
  *   exceeds MOE_SCATTER_NOALLOC_MAX_BYTES, and MOE_EDEVICE when the scratch's
  *   device address cannot be obtained.
  * Every call on one device shares that device's scratch: calls that may run

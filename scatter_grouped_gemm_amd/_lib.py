@@ -28,7 +28,7 @@ SIGNATURES = {
     "moe_compact_rows_bound": (_I64, [_I64, _I32, _I32]),
     "moe_use_masked_layout": (_I32, [_I32, _I32]),
     "moe_choose_layout": (_I32, [_I64, _I32]),
-    "moe_scatter_ws_bytes": (_SZ, [_I32, _I32, _I32]),
+    "moe_scatter_ws_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "moe_status_str": (ctypes.c_char_p, [_I32]),
     "moe_get_device_error": (_I32, [_P, _P, _P]),
     "moe_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
@@ -132,8 +132,8 @@ def moe_choose_layout(max_tokens: int, num_local_experts: int) -> bool:
     return bool(r)
 
 
-def moe_scatter_ws_bytes(T: int, k: int, num_local_experts: int) -> int:
-    return int(lib().moe_scatter_ws_bytes(T, k, num_local_experts))
+def moe_scatter_ws_bytes(T: int, k: int, num_local_experts: int, H: int) -> int:
+    return int(lib().moe_scatter_ws_bytes(T, k, num_local_experts, H))
 
 
 def moe_get_device_error(ws: torch.Tensor) -> int:

@@ -9,10 +9,17 @@
 //   3. rank   : each wavefront walks its chunk in order, 64 assignments at a
 //               time; lanes with the same expert are found with ballots and
 //               ranked by lane order, so rows follow increasing (t, j).  Writes
-//               src2dst.  (compact) m_indices is filled by a grid-stride pass.
+//               src2dst and the assignment of each valid row (src, indexed by
+//               the expert's first valid-row number plus the rank).
+//               (compact) m_indices is filled by a grid-stride pass.
 //   4. rows   : one workgroup per token reads its row once and writes it to
 //               each destination row, optionally quantised to e4m3 with
-//               per-128-channel UE8M0 scales.
+//               per-128-channel UE8M0 scales; the scale bytes are staged
+//               token-major.
+//   5. scales : (FP8) one thread per destination row copies its token's
+//               staged scale bytes into the K-block-major scale array, so
+//               each block's line is written by consecutive threads.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -25,20 +32,27 @@ constexpr int kWsHeader = 256;  // bytes: device error word + padding
 struct ScatterWs {
   int32_t* err;
   int32_t* counts;  // [C][El]
-  int32_t* start;   // [El]
-  int32_t* total;   // [El]
+  int32_t* start;   // [El] first row of expert e (compact; 0 for masked)
+  int32_t* total;   // [El] assignments of expert e
+  int32_t* vstart;  // [El] assignments of the experts before e
+  int32_t* src;     // [A] assignment t*k + j of valid row vstart[e] + rank
+  uint8_t* tscale;  // [T][H/128] FP8: each token's UE8M0 scale bytes
 };
 
 __host__ __device__ inline int64_t num_chunks(int64_t A) { return (A + kChunk - 1) / kChunk; }
 
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-inline size_t ws_bytes(int64_t A, int El) {
+// Scratch of a scatter of T tokens, top-k, El local experts, H channels.
+inline size_t ws_bytes(int64_t T, int k, int El, int H) {
+  const int64_t A = T * k;
   return kWsHeader + align256(static_cast<size_t>(num_chunks(A)) * El * 4) +
-         2 * align256(static_cast<size_t>(El) * 4);
+         3 * align256(static_cast<size_t>(El) * 4) + align256(static_cast<size_t>(A) * 4) +
+         align256(static_cast<size_t>(T) * (H / 128));
 }
 
-inline ScatterWs carve(void* ws, int64_t A, int El) {
+inline ScatterWs carve(void* ws, int64_t T, int k, int El) {
+  const int64_t A = T * k;
   uint8_t* b = static_cast<uint8_t*>(ws);
   ScatterWs w;
   w.err = reinterpret_cast<int32_t*>(b);
@@ -48,6 +62,12 @@ inline ScatterWs carve(void* ws, int64_t A, int El) {
   w.start = reinterpret_cast<int32_t*>(b);
   b += align256(static_cast<size_t>(El) * 4);
   w.total = reinterpret_cast<int32_t*>(b);
+  b += align256(static_cast<size_t>(El) * 4);
+  w.vstart = reinterpret_cast<int32_t*>(b);
+  b += align256(static_cast<size_t>(El) * 4);
+  w.src = reinterpret_cast<int32_t*>(b);
+  b += align256(static_cast<size_t>(A) * 4);
+  w.tscale = b;
   return w;
 }
 
@@ -85,10 +105,12 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
                                                             int El, int block_e, int clamp,
                                                             int32_t* __restrict__ start,
                                                             int32_t* __restrict__ total,
+                                                            int32_t* __restrict__ vstart,
                                                             int32_t* __restrict__ start_out,
                                                             int32_t* __restrict__ valid_out) {
   __shared__ int part[1024];
   __shared__ int64_t wsum[16];
+  __shared__ int64_t wsum_v[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = 1024 / El;
   const int e = tid % El, g = tid / El;
@@ -127,21 +149,34 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
       }
     }
   }
-  // exclusive scan of the padded sizes over the experts (threads tid < El)
+  // exclusive scans of the padded and the plain sizes over the experts
+  // (threads tid < El)
   const int64_t padded = tid < El ? static_cast<int64_t>(run + block_e - 1) / block_e * block_e : 0;
-  int64_t incl = padded;
+  const int64_t plain = tid < El ? run : 0;
+  int64_t incl = padded, incl_v = plain;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int64_t v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
+    const int64_t vv = __shfl_up(incl_v, off, 64);
+    if (lane >= off) {
+      incl += v;
+      incl_v += vv;
+    }
   }
-  if (lane == 63) wsum[w] = incl;
+  if (lane == 63) {
+    wsum[w] = incl;
+    wsum_v[w] = incl_v;
+  }
   __syncthreads();
-  for (int q = 0; q < w; ++q) incl += wsum[q];
+  for (int q = 0; q < w; ++q) {
+    incl += wsum[q];
+    incl_v += wsum_v[q];
+  }
   if (tid < El) {
     const int32_t st = static_cast<int32_t>(incl - padded);
     start[tid] = st;
     total[tid] = run;
+    vstart[tid] = static_cast<int32_t>(incl_v - plain);
     if (start_out) start_out[tid] = st;
     if (valid_out) valid_out[tid] = static_cast<int32_t>(clamp > 0 && run > clamp ? clamp : run);
   }
@@ -150,8 +185,9 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
 template <bool MASKED>
 __global__ __launch_bounds__(256) void scatter_rank_kernel(
     const int32_t* __restrict__ ids, int64_t A, int expert_start, int El, int C,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ start, int max_m,
-    int32_t* __restrict__ src2dst, int32_t* __restrict__ err) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ start,
+    const int32_t* __restrict__ vstart, int max_m, int32_t* __restrict__ src2dst,
+    int32_t* __restrict__ src, int32_t* __restrict__ err) {
   extern __shared__ int lds_i[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + w;
@@ -188,6 +224,8 @@ __global__ __launch_bounds__(256) void scatter_rank_kernel(
     if (valid) {
       int out = -1;
       if (local) {
+        // rank of the assignment inside its expert
+        const int re = MASKED ? r : r - start[key];
         if (!MASKED) {
           out = r;
         } else if (r < max_m) {
@@ -195,6 +233,7 @@ __global__ __launch_bounds__(256) void scatter_rank_kernel(
         } else {
           atomicOr(err, MOE_DEVERR_MASKED_OVERFLOW);
         }
+        if (out >= 0) src[vstart[key] + re] = static_cast<int32_t>(a);
       }
       src2dst[a] = out;
     }
@@ -209,15 +248,23 @@ __global__ __launch_bounds__(256) void scatter_rank_kernel(
 constexpr int kSmallWaves = 16;
 constexpr int64_t kSmallA = 16384;  // assignments handled by the one-workgroup path
 
+// dynamic LDS of the one-workgroup kernel for El local experts
+constexpr size_t small_lds_bytes(int El) {
+  return (static_cast<size_t>(kSmallWaves) * El + 2 * 1024 + 2 * static_cast<size_t>(El)) * sizeof(int);
+}
+
 template <bool MASKED>
 __global__ __launch_bounds__(1024) void scatter_front_small_kernel(
     const int32_t* __restrict__ ids, int A, int expert_start, int El, int block_e, int max_m,
-    int32_t* __restrict__ start, int32_t* __restrict__ total, int32_t* __restrict__ start_out,
-    int32_t* __restrict__ valid_out, int32_t* __restrict__ src2dst, int32_t* __restrict__ err) {
+    int32_t* __restrict__ start, int32_t* __restrict__ total, int32_t* __restrict__ vstart,
+    int32_t* __restrict__ start_out, int32_t* __restrict__ valid_out,
+    int32_t* __restrict__ src2dst, int32_t* __restrict__ src, int32_t* __restrict__ err) {
   extern __shared__ int lds_i[];
   int* const cnt = lds_i;                          // [kSmallWaves][El]
   int* const scan = lds_i + kSmallWaves * El;      // [1024]
-  int* const st_l = scan + 1024;                   // [El]
+  int* const scan_v = scan + 1024;                 // [1024]
+  int* const st_l = scan_v + 1024;                 // [El]
+  int* const vs_l = st_l + El;                     // [El]
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int per = (A + kSmallWaves * 64 - 1) / (kSmallWaves * 64) * 64;
   const int a0 = w * per, a1 = a0 + per < A ? a0 + per : A;
@@ -238,19 +285,25 @@ __global__ __launch_bounds__(1024) void scatter_front_small_kernel(
     }
   }
   const int padded = tid < El ? (run + block_e - 1) / block_e * block_e : 0;
+  const int plain = tid < El ? run : 0;
   scan[tid] = padded;
+  scan_v[tid] = plain;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int v = tid >= off ? scan[tid - off] : 0;
+    const int vv = tid >= off ? scan_v[tid - off] : 0;
     __syncthreads();
     scan[tid] += v;
+    scan_v[tid] += vv;
     __syncthreads();
   }
   if (tid < El) {
     const int st = scan[tid] - padded;
     st_l[tid] = st;
+    vs_l[tid] = scan_v[tid] - plain;
     start[tid] = st;
     total[tid] = run;
+    vstart[tid] = scan_v[tid] - plain;
     if (start_out) start_out[tid] = st;
     if (valid_out) valid_out[tid] = MASKED && run > max_m ? max_m : run;
   }
@@ -286,6 +339,7 @@ __global__ __launch_bounds__(1024) void scatter_front_small_kernel(
     if (valid) {
       int out = -1;
       if (local) {
+        const int re = MASKED ? r : r - st_l[key];
         if (!MASKED) {
           out = r;
         } else if (r < max_m) {
@@ -293,6 +347,7 @@ __global__ __launch_bounds__(1024) void scatter_front_small_kernel(
         } else {
           atomicOr(err, MOE_DEVERR_MASKED_OVERFLOW);
         }
+        if (out >= 0) src[vs_l[key] + re] = a;
       }
       src2dst[a] = out;
     }
@@ -330,10 +385,14 @@ __device__ __forceinline__ int64_t scale_index(int64_t row, int b, int64_t ld, i
   return (g * HB + b) * max_m + (row - g * max_m);
 }
 
+// Step 4: the token's row, read once, copied (or quantised, FP8) to each of
+// its destination rows.  FP8 scale bytes go to the token-major staging array
+// tscale[t][H/128] (56 contiguous bytes per token instead of k * 56 scattered
+// ones); scatter_scales_kernel moves them to the destination layout.
 template <bool FP8>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(
     const uint16_t* __restrict__ x, int H, int k, const int32_t* __restrict__ src2dst,
-    uint8_t* __restrict__ x_out, uint8_t* __restrict__ scale_out, int64_t scale_ld, int max_m) {
+    uint8_t* __restrict__ x_out, uint8_t* __restrict__ tscale) {
   __shared__ int rows[32];
   const int t = blockIdx.x;
   if (threadIdx.x < k) rows[threadIdx.x] = src2dst[static_cast<int64_t>(t) * k + threadIdx.x];
@@ -374,15 +433,45 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
         const uint32_t lo = e4m3x4(f[0], f[1], f[2], f[3], e);
         const uint32_t hi = e4m3x4(f[4], f[5], f[6], f[7], e);
         const uint2 q = make_uint2(lo, hi);
-        const bool leader = (threadIdx.x & 15) == 0;
+        if ((threadIdx.x & 15) == 0)
+          tscale[static_cast<int64_t>(t) * HB + col / 128] = static_cast<uint8_t>(e + 127);
         for (int j = 0; j < k; ++j) {
           const int r = rows[j];
           if (r < 0) continue;
           *reinterpret_cast<uint2*>(x_out + static_cast<int64_t>(r) * H + col) = q;
-          if (leader) scale_out[scale_index(r, col / 128, scale_ld, max_m, HB)] = static_cast<uint8_t>(e + 127);
         }
       }
     }
+  }
+}
+
+// FP8 scale bytes in the destination layout, one thread per destination row
+// (consecutive threads write consecutive bytes of each 128-channel block's
+// scale line): valid row r of expert e has rank r_e inside e; its token is
+// src[vstart[e] + r_e] / k, whose staged bytes are copied.  Compact rows take
+// e from m_indices (padding rows are skipped); masked row r belongs to group
+// r / max_m and is valid below min(total, max_m).
+template <bool MASKED>
+__global__ __launch_bounds__(256) void scatter_scales_kernel(
+    const int32_t* __restrict__ m_indices, const int32_t* __restrict__ start,
+    const int32_t* __restrict__ total, const int32_t* __restrict__ vstart,
+    const int32_t* __restrict__ src, const uint8_t* __restrict__ tscale, int k, int HB,
+    int64_t rows, int max_m, uint8_t* __restrict__ scale_out) {
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < rows;
+       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int e, re;
+    if (MASKED) {
+      e = static_cast<int>(r / max_m);
+      re = static_cast<int>(r - static_cast<int64_t>(e) * max_m);
+      if (re >= min(total[e], max_m)) continue;
+    } else {
+      e = m_indices[r];
+      if (e < 0) continue;
+      re = static_cast<int>(r - start[e]);
+    }
+    const int64_t t = src[vstart[e] + re] / k;
+    const uint8_t* ts = tscale + t * HB;
+    for (int b = 0; b < HB; ++b) scale_out[scale_index(r, b, rows, MASKED ? max_m : 0, HB)] = ts[b];
   }
 }
 
@@ -398,8 +487,9 @@ int32_t validate_common(const void* x, int32_t T, int32_t H, const int32_t* ids,
   return MOE_OK;
 }
 
-int32_t validate_ws(int32_t T, int32_t k, int32_t El, const void* ws, size_t ws_bytes_given) {
-  if (!ws || ws_bytes_given < ws_bytes(static_cast<int64_t>(T) * k, El)) return MOE_ECAPACITY;
+int32_t validate_ws(int32_t T, int32_t k, int32_t El, int32_t H, const void* ws,
+                    size_t ws_bytes_given) {
+  if (!ws || ws_bytes_given < ws_bytes(T, k, El, H)) return MOE_ECAPACITY;
   return MOE_OK;
 }
 
@@ -407,9 +497,9 @@ int32_t validate_ws(int32_t T, int32_t k, int32_t El, const void* ws, size_t ws_
 
 using namespace moe;
 
-extern "C" size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts) {
-  if (T < 0 || k < 1 || num_local_experts < 1) return 0;
-  return ws_bytes(static_cast<int64_t>(T) * k, num_local_experts);
+extern "C" size_t moe_scatter_ws_bytes(int32_t T, int32_t k, int32_t num_local_experts, int32_t H) {
+  if (T < 0 || k < 1 || num_local_experts < 1 || H < 0) return 0;
+  return ws_bytes(T, k, num_local_experts, H);
 }
 
 extern "C" int64_t moe_compact_rows_bound(int64_t A, int32_t E, int32_t block_e) {
@@ -434,7 +524,7 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
                             int32_t* valid_out, bool masked, int32_t max_m, int32_t* src2dst,
                             hipStream_t s) {
   if (A <= kSmallA) {
-    const size_t lds = (static_cast<size_t>(kSmallWaves) * El + 1024 + El) * sizeof(int);
+    const size_t lds = small_lds_bytes(El);
     // The LDS limit is raised once per device and layout (thread-safe).
     static std::once_flag attr_once[64][2];
     static bool attr_ok[64][2] = {};
@@ -446,13 +536,12 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
       attr_ok[dev][li] =
           hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>((static_cast<size_t>(kSmallWaves) + 1) * 1024 * sizeof(int) +
-                                               1024 * sizeof(int))) == hipSuccess;
+                              static_cast<int>(small_lds_bytes(1024))) == hipSuccess;
     });
     if (!attr_ok[dev][li]) return MOE_EDEVICE;
     kern<<<1, 1024, lds, s>>>(ids, static_cast<int>(A), expert_start, El, masked ? 1 : block_e,
-                              masked ? max_m : 0, w.start, w.total, start_out, valid_out, src2dst,
-                              w.err);
+                              masked ? max_m : 0, w.start, w.total, w.vstart, start_out, valid_out,
+                              src2dst, w.src, w.err);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }
@@ -466,22 +555,23 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
   }
   MOE_CHECK_LAUNCH();
   scatter_scan_kernel<<<1, 1024, 0, s>>>(w.counts, C, El, masked ? 1 : block_e, masked ? max_m : 0,
-                                         w.start, w.total, start_out, valid_out);
+                                         w.start, w.total, w.vstart, start_out, valid_out);
   MOE_CHECK_LAUNCH();
   if (C > 0) {
     if (masked)
       scatter_rank_kernel<true><<<nb, 256, lds, s>>>(ids, A, expert_start, El, C, w.counts,
-                                                     w.start, max_m, src2dst, w.err);
+                                                     w.start, w.vstart, max_m, src2dst, w.src,
+                                                     w.err);
     else
       scatter_rank_kernel<false><<<nb, 256, lds, s>>>(ids, A, expert_start, El, C, w.counts,
-                                                      w.start, 0, src2dst, w.err);
+                                                      w.start, w.vstart, 0, src2dst, w.src, w.err);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
 }
 
 // Everything after argument validation of the compact scatter: the workspace
-// `ws` (at least ws_bytes(T*k, El) bytes) is supplied by the caller or is the
+// `ws` (at least ws_bytes(T, k, El, H) bytes) is supplied by the caller or is the
 // library's static scratch array.
 static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const int32_t* topk_ids,
                                     int32_t k, int32_t expert_start, int32_t El, int32_t block_e,
@@ -490,7 +580,7 @@ static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const i
                                     int32_t* expert_start_loc, int32_t* num_valid,
                                     int32_t* src2dst, void* ws, hipStream_t s) {
   const int64_t A = static_cast<int64_t>(T) * k;
-  const ScatterWs w = carve(ws, A, El);
+  const ScatterWs w = carve(ws, T, k, El);
   int32_t st = launch_front(topk_ids, A, expert_start, El, block_e, w, expert_start_loc, num_valid, false, 0,
                     src2dst, s);
   if (st != MOE_OK) return st;
@@ -502,14 +592,21 @@ static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const i
     MOE_CHECK_LAUNCH();
   }
   if (T > 0) {
-    if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+    const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+    if (fp8)
       scatter_rows_kernel<true><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
-                                                  static_cast<uint8_t*>(x_out), scale_out,
-                                                  rows_capacity, 0);
+                                                  static_cast<uint8_t*>(x_out), w.tscale);
     else
       scatter_rows_kernel<false><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
-                                                   static_cast<uint8_t*>(x_out), nullptr, 0, 0);
+                                                   static_cast<uint8_t*>(x_out), nullptr);
     MOE_CHECK_LAUNCH();
+    if (fp8 && rows_capacity > 0) {
+      const int64_t nb = std::min<int64_t>((rows_capacity + 255) / 256, 2048);
+      scatter_scales_kernel<false><<<static_cast<int>(nb), 256, 0, s>>>(
+          m_indices, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows_capacity, 0,
+          scale_out);
+      MOE_CHECK_LAUNCH();
+    }
   }
   return MOE_OK;
 }
@@ -534,7 +631,7 @@ extern "C" int32_t moe_scatter_compact(const void* x, int32_t T, int32_t H, cons
                                        void* stream) {
   int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst);
   if (st != MOE_OK) return st;
-  st = validate_ws(T, k, El, ws, ws_bytes_given);
+  st = validate_ws(T, k, El, H, ws, ws_bytes_given);
   if (st != MOE_OK) return st;
   st = validate_compact(T, k, El, block_e, rows_capacity, m_indices, expert_start_loc, num_valid);
   if (st != MOE_OK) return st;
@@ -581,7 +678,7 @@ extern "C" int32_t moe_scatter_compact_noalloc(const void* x, int32_t T, int32_t
   if (st != MOE_OK) return st;
   st = validate_compact(T, k, El, block_e, rows_capacity, m_indices, expert_start_loc, num_valid);
   if (st != MOE_OK) return st;
-  if (ws_bytes(static_cast<int64_t>(T) * k, El) > MOE_SCATTER_NOALLOC_MAX_BYTES) return MOE_ECAPACITY;
+  if (ws_bytes(T, k, El, H) > MOE_SCATTER_NOALLOC_MAX_BYTES) return MOE_ECAPACITY;
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st != MOE_OK) return st;
@@ -599,24 +696,32 @@ extern "C" int32_t moe_scatter_masked(const void* x, int32_t T, int32_t H, const
                                       size_t ws_bytes_given, void* stream) {
   int32_t st = validate_common(x, T, H, topk_ids, k, El, out_dtype, x_out, scale_out, src2dst);
   if (st != MOE_OK) return st;
-  st = validate_ws(T, k, El, ws, ws_bytes_given);
+  st = validate_ws(T, k, El, H, ws, ws_bytes_given);
   if (st != MOE_OK) return st;
   if (!masked_m || max_m <= 0) return MOE_EINVAL;
   if (max_m < T) return MOE_ECAPACITY;
   if (static_cast<int64_t>(El) * max_m >= (1ll << 31)) return MOE_EINVAL;
   const int64_t A = static_cast<int64_t>(T) * k;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const ScatterWs w = carve(ws, A, El);
+  const ScatterWs w = carve(ws, T, k, El);
   st = launch_front(topk_ids, A, expert_start, El, 1, w, nullptr, masked_m, true, max_m, src2dst, s);
   if (st != MOE_OK) return st;
   if (T > 0) {
-    if (out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0)
+    const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+    if (fp8)
       scatter_rows_kernel<true><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
-                                                  static_cast<uint8_t*>(x_out), scale_out, 0, max_m);
+                                                  static_cast<uint8_t*>(x_out), w.tscale);
     else
       scatter_rows_kernel<false><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
-                                                   static_cast<uint8_t*>(x_out), nullptr, 0, max_m);
+                                                   static_cast<uint8_t*>(x_out), nullptr);
     MOE_CHECK_LAUNCH();
+    if (fp8) {
+      const int64_t rows = static_cast<int64_t>(El) * max_m;
+      const int64_t nb = std::min<int64_t>((rows + 255) / 256, 2048);
+      scatter_scales_kernel<true><<<static_cast<int>(nb), 256, 0, s>>>(
+          nullptr, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows, max_m, scale_out);
+      MOE_CHECK_LAUNCH();
+    }
   }
   return MOE_OK;
 }

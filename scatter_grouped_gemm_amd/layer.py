@@ -82,7 +82,7 @@ class MoELayer:
         else:
             self.m_indices = None
             self.masked_m = torch.empty(El, dtype=torch.int32, device=d)
-        ws_bytes = L.moe_scatter_ws_bytes(T, k, El)
+        ws_bytes = L.moe_scatter_ws_bytes(T, k, El, H)
         self.ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.int32, device=d)
         self.w13 = self.w2 = self.w13_scale = self.w2_scale = None
         # optional timing: name -> list of (start, end) HIP events recorded on

@@ -56,10 +56,16 @@ def test_status_strings():
 
 
 def test_ws_bytes_grow_with_problem():
-    a = L.moe_scatter_ws_bytes(64, 2, 8)
-    b = L.moe_scatter_ws_bytes(16384, 8, 128)
-    assert 0 < a < b
-    assert L.lib().moe_scatter_ws_bytes(-1, 2, 8) == 0
+    a = L.moe_scatter_ws_bytes(64, 2, 8, 256)
+    b = L.moe_scatter_ws_bytes(16384, 8, 128, 256)
+    c = L.moe_scatter_ws_bytes(16384, 8, 128, 7168)
+    assert 0 < a < b < c
+    # at least the per-row assignment index (4 bytes per assignment) and one
+    # staged scale byte per token and 128 channels
+    assert c - b >= 16384 * (7168 - 256) // 128
+    assert b >= 16384 * 8 * 4
+    assert L.lib().moe_scatter_ws_bytes(-1, 2, 8, 256) == 0
+    assert L.lib().moe_scatter_ws_bytes(4, 2, 8, -128) == 0
 
 
 def test_validation_rejects_before_launch():
@@ -70,7 +76,7 @@ def test_validation_rejects_before_launch():
     assert lib.moe_route_topk(P, 4, 8, 9, P, P, None) == L.MOE_EINVAL          # k > E
     assert lib.moe_route_topk(P, 4, 2048, 8, P, P, None) == L.MOE_EINVAL       # E > 1024
     assert lib.moe_route_topk(None, 4, 8, 2, P, P, None) == L.MOE_EINVAL
-    ws = L.moe_scatter_ws_bytes(64, 2, 8)
+    ws = L.moe_scatter_ws_bytes(64, 2, 8, 256)
     # compact scatter: capacity below the bound, H not a multiple of 128, block_e, ws too small
     bound = L.moe_compact_rows_bound(128, 8, 128)
     args = lambda T, H, El, be, R, dt, wsb: (P, T, H, P, 2, 0, El, be, R, dt, P, P, P, P, P, P, P, wsb, None)
@@ -182,7 +188,7 @@ def test_noalloc_scatter_validates_before_device_work():
     assert lib.moe_scatter_compact_noalloc(*args(64, 256, 2, 0, 128, bound)) == L.MOE_EINVAL
     # 2^23 assignments over 256 experts need more than the 4 MiB static scratch
     T, k, El = 1 << 20, 8, 256
-    assert L.moe_scatter_ws_bytes(T, k, El) > L.MOE_SCATTER_NOALLOC_MAX_BYTES
+    assert L.moe_scatter_ws_bytes(T, k, El, 128) > L.MOE_SCATTER_NOALLOC_MAX_BYTES
     R = L.moe_compact_rows_bound(T * k, El, 128)
     assert lib.moe_scatter_compact_noalloc(*args(T, 128, k, El, 128, R)) == L.MOE_ECAPACITY
     # the limit the header states

@@ -86,7 +86,7 @@ def test_scatter_compact(orc, T, H, E, El, start, k, fp8):
     st = poison((El,), torch.int32)
     nv = poison((El,), torch.int32)
     s2d = poison((T, k), torch.int32)
-    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El, H), dtype=torch.uint8, device=DEV)
     L.moe_scatter_compact(x.to(DEV), i32_dev(ids), start, El, 128, R, fp8, x_out, s_out, m_idx, st,
                           nv, s2d, ws)
     torch.cuda.synchronize()
@@ -116,7 +116,7 @@ def test_scatter_masked(orc, T, H, E, El, start, k, fp8):
     s_out = poison((El, H // 128, max_m), torch.uint8) if fp8 else None
     mm = poison((El,), torch.int32)
     s2d = poison((T, k), torch.int32)
-    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El, H), dtype=torch.uint8, device=DEV)
     L.moe_scatter_masked(x.to(DEV), i32_dev(ids), start, El, max_m, fp8, x_out, s_out, mm, s2d, ws)
     torch.cuda.synchronize()
     assert np.array_equal(mm.cpu().numpy(), ref["masked_m"])
@@ -138,7 +138,7 @@ def test_scatter_masked_overflow_flag(orc):
     T, H, k, El = 4, 128, 3, 4
     ids = np.array([[1, 1, 1], [1, 2, 3], [1, 0, 2], [1, 1, 0]], np.int32)
     x = torch.randn(T, H, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
-    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El, H), dtype=torch.uint8, device=DEV)
     s2d = poison((T, k), torch.int32)
     mm = poison((El,), torch.int32)
     L.moe_scatter_masked(x.to(DEV), i32_dev(ids), 0, El, T, False, poison((El * T, H), torch.bfloat16),

@@ -26,7 +26,7 @@ def _outputs(T, H, E, El, start, k, fp8, seed, noalloc):
     if noalloc:
         L.moe_scatter_compact_noalloc(*args)
     else:
-        ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El), dtype=torch.uint8, device=DEV)
+        ws = torch.empty(L.moe_scatter_ws_bytes(T, k, El, H), dtype=torch.uint8, device=DEV)
         L.moe_scatter_compact(*args, ws)
     torch.cuda.synchronize()
     return {n: (t.view(torch.uint8).cpu().numpy() if t is not None and t.dtype == torch.bfloat16
@@ -61,7 +61,7 @@ def test_noalloc_matches_workspace_entry(first, second, fp8):
 
 def test_noalloc_rejects_oversize():
     T, k, El = 1 << 20, 8, 256
-    assert L.moe_scatter_ws_bytes(T, k, El) > L.MOE_SCATTER_NOALLOC_MAX_BYTES
+    assert L.moe_scatter_ws_bytes(T, k, El, 128) > L.MOE_SCATTER_NOALLOC_MAX_BYTES
     x = torch.empty(1, 128, dtype=torch.bfloat16, device=DEV)
     P = x.data_ptr()
     st = L.lib().moe_scatter_compact_noalloc(P, T, 128, P, k, 0, El, 128, 1 << 30, 0, P, None, P,
