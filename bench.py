@@ -132,7 +132,7 @@ def roofline(flops, nbytes, ms, dtype):
 
 # the sources the grouped-GEMM kernels are built from: counter figures taken
 # on other sources are not reported
-GEMM_SOURCES = ("gemm.hip", "gemm_wreg.hip", "gemm_wreg.h", "common.h")
+GEMM_SOURCES = ("gemm.hip", "gemm_wreg.hip", "gemm_wreg.h", "gemm_runs.h", "common.h")
 
 
 def gemm_source_sha256():

@@ -625,7 +625,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
   // of the 128-byte k-step, so the instruction's k order is the memory order
   // and an MX scale byte per lane covers one contiguous 32-block.  With one
   // scale per 128-wide k-step the order is free, and chunks 2g, 2g + 1 read
-  // about 3% faster (measured), so those kernels keep them.
+  // about 3% faster (measured), so those kernels keep them.  BF16: the two
+  // 16x16x32 MFMAs of a k-step take chunks 2g and 2g + 1 (even, then odd), the
+  // order of the register-streamed kernel too, so a row's sums come out
+  // bit-identical whichever kernel or layout computes them.
   using frag_t = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
   constexpr int KS = FP8 ? 1 : 2;  // MFMA k-substeps per 128-byte stage
   struct Frags {
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
           F_.a[ks][im] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
                                  (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
         } else {                                                                                 \
-          F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+          F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, 2 * frag_k + ks)); \
         }                                                                                        \
       }                                                                                          \
       _Pragma("unroll") for (int jn = 0; jn < TN; ++jn) {                                        \
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
           F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
                                  (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
         } else {                                                                                 \
-          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, 2 * frag_k + ks)); \
         }                                                                                        \
       }                                                                                          \
     }                                                                                            \
@@ -691,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
       F_.a[ks][im] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],                 \
                              (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};                \
     } else {                                                                                     \
-      F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, (ks) * 4 + frag_k));  \
+      F_.a[ks][im] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, 2 * frag_k + (ks)));  \
     }                                                                                            \
   } while (0)
 // The weight fragments and the scales of stage st_.
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
           F_.b[ks][jn] = i32x8_t{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3],             \
                                  (int)hi_[0], (int)hi_[1], (int)hi_[2], (int)hi_[3]};            \
         } else {                                                                                 \
-          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, ks * 4 + frag_k)); \
+          F_.b[ks][jn] = *reinterpret_cast<const frag_t*>(S_ + MOE_ROWOFF(rb_, 2 * frag_k + ks)); \
         }                                                                                        \
       }                                                                                          \
     }                                                                                            \

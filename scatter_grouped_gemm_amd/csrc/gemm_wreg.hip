@@ -11,20 +11,19 @@
 //     bytes it keeps in flight.  Staging the weights through LDS caps that at a
 //     few 48 KB stages; here every wavefront loads its own weight columns
 //     straight into VGPRs in MFMA fragment order (buffer_load_dwordx4), four
-//     k-steps ahead, so a CU keeps 128 KB of weights plus four 24 KB
+//     k-steps ahead, so a CU keeps 128 KB of weights plus four 32 KB
 //     activation stages in flight.
 //   - Workgroup = 4 wavefronts (one per SIMD, 512 registers each).  A tile is
-//     up to 192 rows of one expert run by 256 weight columns; wavefront w owns
+//     up to 256 rows of one expert run by 256 weight columns; wavefront w owns
 //     64 columns and all rows, so the activations (shared by every wavefront)
 //     go through LDS once (direct-to-LDS buffer loads, 16 bytes per lane) and
 //     each weight byte sits in exactly one wavefront's registers.  LDS reads
 //     per k-step are 64 bytes per MFMA cycle, half the LDS bandwidth.
 //   - Tiles follow the expert runs of the compact layout rather than its
-//     128-row blocks: a run of c valid rows is cut into ceil(128 nb / 192)
-//     tiles (nb = its 128-row blocks) of equal height rounded up to 16, and
-//     only the 16-row blocks holding rows run MFMAs.  An expert with 257-384
-//     rows therefore costs two passes over its weights, not three, and no tile
-//     computes a whole padding block.
+//     128-row blocks: a run of z valid rows is cut into ceil(z / 256) tiles of
+//     equal height rounded up to 16 (gemm_runs.h), and only the 16-row blocks
+//     holding rows run MFMAs.  An expert with up to 256 rows streams its
+//     weights once, and no tile computes a whole padding block.
 //   - A k-step is 128 bytes of a row (128 e4m3 or 64 bf16).  MFMA: the block-
 //     scaled v_mfma_scale_f32_16x16x128_f8f6f4 (the UE8M0 bytes are its E8M0
 //     scale operands: the 128-channel activation scale and the 128x128 weight
@@ -56,6 +55,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_runs.h"
 #include "gemm_wreg.h"
 
 namespace moe {
@@ -73,9 +73,12 @@ constexpr int kMT = kRB * 16;               // tile rows at most
 constexpr int kNS = 4;                      // LDS stages = weight register sets
 constexpr int kLA = kNS - 1;                // k-steps of lookahead
 constexpr int kALD = kMT * 128 / 1024 / 4;  // activation loads per wavefront per step
-constexpr int kTable = 1024;                // run-table entries (one XCD's share)
-constexpr int kGM = 8;                      // M-tiles of a group in the tile order
-constexpr int kMaxBlocks = 8160;            // 128-row blocks of A (about a million rows)
+using runs::decode;
+using runs::kMaxBlocks;
+using runs::kTable;
+using runs::lds_off;
+using runs::Tile;
+using runs::wait_vm;
 constexpr int kActBytes = kMT * 128;
 static_assert(kALD * 4 * 1024 == kActBytes, "whole 1 KB loads per wavefront");
 
@@ -93,10 +96,14 @@ constexpr int lds_bytes() {
 template <bool FP8>
 constexpr int vm_per_step() { return kALD + (FP8 ? 2 : 0) + 8; }
 
-// MFMA operand fragments of one 128-byte k-step: FP8 one 32-byte operand of
-// the 16x16x128 instruction (k order = memory order: chunk g, then chunk g+4
-// of lane group g); BF16 the two 16-byte operands of two 16x16x32
-// instructions (chunks g and g + 4).
+// MFMA operand fragments of one 128-byte k-step: lane group g (lanes 16 g ..
+// 16 g + 15) holds 16-byte chunks 2 g and 2 g + 1 of its row, 32 contiguous
+// bytes.  FP8: one 32-byte operand of the 16x16x128 instruction (k order =
+// memory order).  BF16: the two 16-byte operands of two 16x16x32
+// instructions, the first over the even chunks of the row and the second over
+// the odd ones; both operands use the same order, so together they form the
+// whole dot product, and the contiguous 32-byte LDS reads avoid the bank
+// conflicts that chunks g and g + 4 would cause.
 struct Bf16Frag {
   u32x4 lo, hi;
 };
@@ -195,7 +202,6 @@ __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 }
 
-// M-tiles of a run of nb 128-row blocks
 // The loads of one k-step are spread over the row blocks of the step before
 // (one piece after each block, at most): the texture unit that every vector
 // memory instruction of the CU passes through is the busiest part of the
@@ -205,29 +211,6 @@ __device__ __forceinline__ void mfma_drain() {
 // activation row group j (j < 8; FP8: 12 the activation scales, 13 the
 // weight scales), -1 nothing.  Column block 0 is loaded in block 0.
 constexpr int kLoadAt[kRB] = {-1, 4, 1, 5, 6, 2, 7, 12, 8, 3, 9, 10, 13, 11, -1, -1};
-
-// M-tiles of a run with z valid rows: as few as the tile height allows, so an
-// expert with at most 256 rows is one tile and its weights stream once
-__device__ __forceinline__ int tiles_of(int z) { return (z + kMT - 1) / kMT; }
-
-// vmcnt <= N, lgkmcnt 0 (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-}
-// Run-table reads are hand-written: the compiler would otherwise order them
-// after every outstanding direct-to-LDS load, which never touches the table.
-__device__ __forceinline__ int4 lds_read_run(const int4* t) {
-  int4 v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(t)) : "memory");
-  return v;
-}
 
 __device__ __forceinline__ void lds_write_f32(float* p, float v) {
   asm volatile("ds_write_b32 %0, %1" : : "v"(lds_off(p)), "v"(v) : "memory");
@@ -241,92 +224,6 @@ __device__ __forceinline__ f32x4 lds_read_f32x4(const float* p) {
 // chunk permutation of activation stage row r: the 16 lanes reading one
 // 16-byte chunk of 16 consecutive rows hit distinct banks
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// exclusive scans over the workgroup's 256 threads (scr: 8 ints of LDS)
-__device__ __forceinline__ int scan_excl_max(int v, int* scr) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off, 64);
-    if (lane >= off) inc = max(inc, o);
-  }
-  if (lane == 63) scr[w] = inc;
-  __syncthreads();
-  int ex = __shfl_up(inc, 1, 64);
-  if (lane == 0) ex = INT_MIN;
-  for (int q = 0; q < w; ++q) ex = max(ex, scr[q]);
-  __syncthreads();
-  return ex;
-}
-__device__ __forceinline__ int2 scan_excl_sum2(int a, int b, int* scr, int2& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int oa = __shfl_up(ia, off, 64), ob = __shfl_up(ib, off, 64);
-    if (lane >= off) {
-      ia += oa;
-      ib += ob;
-    }
-  }
-  if (lane == 63) {
-    scr[2 * w] = ia;
-    scr[2 * w + 1] = ib;
-  }
-  __syncthreads();
-  int pa = 0, pb = 0, ta = 0, tb = 0;
-  for (int q = 0; q < 4; ++q) {
-    if (q < w) {
-      pa += scr[2 * q];
-      pb += scr[2 * q + 1];
-    }
-    ta += scr[2 * q];
-    tb += scr[2 * q + 1];
-  }
-  __syncthreads();
-  total = make_int2(ta, tb);
-  return make_int2(pa + ia - a, pb + ib - b);
-}
-
-// A tile: rows [row, row + rows) of A/C, expert id, N-tile nt
-struct Tile {
-  int64_t row;
-  int rows, id, nt;
-};
-
-// Position pos of the order -> tile (rows <= 0: an empty position).  Run-table
-// entries (P = first position, first row, valid rows, expert) are sorted by P;
-// the cursor only moves forward since a workgroup's positions increase.
-__device__ __forceinline__ Tile decode(const int4* table, int nr, int& cur, int pos, int ntn) {
-  int4 r;
-  int nt;
-  for (;;) {
-    r = lds_read_run(table + cur);
-    r.x = __builtin_amdgcn_readfirstlane(r.x);
-    r.y = __builtin_amdgcn_readfirstlane(r.y);
-    r.z = __builtin_amdgcn_readfirstlane(r.z);
-    r.w = __builtin_amdgcn_readfirstlane(r.w);
-    nt = tiles_of(r.z);
-    if (pos < r.x + nt * ntn || cur + 1 >= nr) break;
-    ++cur;
-  }
-  Tile t;
-  const int q = pos - r.x;
-  const int mg = q / (kGM * ntn);
-  const int m0 = mg * kGM;
-  const int gsz = min(kGM, nt - m0);
-  const int rest = q - mg * kGM * ntn;
-  const int ntile = gsz > 0 ? rest / gsz : 0;
-  const int m = m0 + rest - ntile * gsz;
-  const int h = ((r.z + nt - 1) / nt + 15) & ~15;
-  const int r0 = m * h;
-  t.rows = (q < 0 || q >= nt * ntn || gsz <= 0) ? 0 : min(h, r.z - r0);
-  t.row = static_cast<int64_t>(r.y) + r0;
-  t.id = r.w;
-  t.nt = ntile;
-  return t;
-}
 
 template <bool FP8, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p) {
@@ -348,95 +245,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   const int I = p.N / 2;
 
   // ======== set-up: the run table of this XCD's share of the order ========
-  const int nblk = static_cast<int>((p.M + 127) / 128);
-  int* const ids = reinterpret_cast<int*>(smem);  // [nblk] first-row ids (stage memory)
-  int* const scr = ids + kMaxBlocks + 8;
-  int* const zv = scr + 16;  // [nblk] valid rows of the run ending at block j
-  static_assert((2 * kMaxBlocks + 24) * 4 <= kNS * kActBytes, "set-up arrays fit in the stages");
-  for (int j = tid; j < nblk; j += kThreads) {
-    const int v = p.m_indices[static_cast<int64_t>(j) * 128];
-    ids[j] = (v >= 0 && v < p.G) ? v : -1;
-  }
-  __syncthreads();
-  const int PB = (nblk + kThreads - 1) / kThreads;
-  const int j0 = min(tid * PB, nblk), j1 = min(j0 + PB, nblk);
-  // block j starts a run if its id differs from the block before; ends one if
-  // the block after differs
-  int ls = -1;
-  for (int j = j0; j < j1; ++j)
-    if (ids[j] >= 0 && (j == 0 || ids[j - 1] != ids[j])) ls = j;
-  const int carry = max(scan_excl_max(ls, scr), -1);
-  // runs ending in this thread's blocks: their valid rows (the last block's
-  // valid rows come first, so a binary search for its first negative entry)
-  // and M-tiles
-  int cnt = 0, tsum = 0;
-  {
-    int S = carry;
-    for (int j = j0; j < j1; ++j) {
-      const int v = ids[j];
-      if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
-      if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
-        const int64_t r0 = static_cast<int64_t>(j) * 128;
-        int lo = 1, hi = p.M - r0 < 128 ? static_cast<int>(p.M - r0) : 128;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (p.m_indices[r0 + mid] >= 0) lo = mid + 1;
-          else hi = mid;
-        }
-        const int z = (j - S) * 128 + lo;
-        zv[j] = z;
-        ++cnt;
-        tsum += tiles_of(z);
-      }
-    }
-  }
-  int2 tot;
-  const int2 base = scan_excl_sum2(cnt, tsum, scr, tot);
-  const int U = tot.y * ntn;  // positions of the whole order
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int lo_x = static_cast<int>((static_cast<int64_t>(U) * xcd) >> 3);
-  const int hi_x = static_cast<int>((static_cast<int64_t>(U) * (xcd + 1)) >> 3);
-  // runs ending at or before lo_x, runs starting before hi_x
-  int c_lo = 0, c_hi = 0;
-  {
-    int S = carry, mb = base.y;
-    for (int j = j0; j < j1; ++j) {
-      const int v = ids[j];
-      if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
-      if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
-        const int nt = tiles_of(zv[j]);
-        if ((mb + nt) * ntn <= lo_x) ++c_lo;
-        if (mb * ntn < hi_x) ++c_hi;
-        mb += nt;
-      }
-    }
-  }
-  int2 cc;
-  scan_excl_sum2(c_lo, c_hi, scr, cc);
-  const int R0 = cc.x, NR = cc.y - cc.x;
-  {
-    int S = carry, mb = base.y, ri = base.x;
-    for (int j = j0; j < j1; ++j) {
-      const int v = ids[j];
-      if (v >= 0 && (j == 0 || ids[j - 1] != v)) S = j;
-      if (v >= 0 && (j == nblk - 1 || ids[j + 1] != v)) {
-        const int z = zv[j];
-        const int nt = tiles_of(z);
-        const int P = mb * ntn, Pe = (mb + nt) * ntn;
-        if (Pe > lo_x && P < hi_x && ri - R0 >= 0 && ri - R0 < kTable)
-          table[ri - R0] = make_int4(P, S * 128, z, v);
-        ++ri;
-        mb += nt;
-      }
-    }
-  }
-  __syncthreads();  // table complete; stage memory is free
-  if (NR <= 0 || NR > kTable || lo_x + static_cast<int>(blockIdx.x >> 3) >= hi_x) return;
+  static_assert(runs::kSetupBytes <= kNS * kActBytes, "set-up arrays fit in the stages");
+  runs::Share sh;
+  if (!runs::build_share(p.m_indices, p.M, p.G, ntn, smem, table, sh)) return;
+  const int NR = sh.NR, lo_x = sh.lo, hi_x = sh.hi, per_xcd = sh.per_xcd;
 
   // ======== per-lane constants ========
   const int fr = lane & 15, fg = lane >> 4;
-  // activation loads: wavefront w moves stage rows 8q .. 8q+7 for q = 6w + j;
+  // activation loads: wavefront w moves stage rows 8q .. 8q+7 for q = 8w + j;
   // lane L carries source chunk (L & 7) ^ swz(row) into LDS position L
   uint32_t va[kALD];
 #pragma unroll
@@ -456,11 +272,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
 
   // ======== load side: the tile and k-step whose loads are issued next ========
   int d_cur = 0, d_pos = lo_x + static_cast<int>(blockIdx.x >> 3);
-  Tile dt = decode(table, NR, d_cur, d_pos, ntn);
+  Tile dt = decode<16>(table, NR, d_cur, d_pos, ntn);
   while (dt.rows <= 0) {
     d_pos += per_xcd;
     if (d_pos >= hi_x) return;
-    dt = decode(table, NR, d_cur, d_pos, ntn);
+    dt = decode<16>(table, NR, d_cur, d_pos, ntn);
   }
   int d_k = 0;
   __amdgpu_buffer_rsrc_t rs_a, rs_w;
@@ -480,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
         const_cast<uint8_t*>(p.B + static_cast<int64_t>(dt.id) * p.N * rowbytes), 0,
         static_cast<int>(static_cast<int64_t>(p.N) * rowbytes), 0x00020000);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) vw[cb] = static_cast<uint32_t>(wrow(cb, dt.nt) * rowbytes + fg * (FP8 ? 32 : 16));
+    for (int cb = 0; cb < 4; ++cb) vw[cb] = static_cast<uint32_t>(wrow(cb, dt.nt) * rowbytes + fg * 32);
     wbase8 = p.B + static_cast<int64_t>(dt.id) * p.N * rowbytes;
     if constexpr (FP8) {
       const int r = min(wave * 64 + lane, dt.rows - 1);
@@ -506,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       w[cb] = *reinterpret_cast<const i32x8*>(wbase8 + d_k * 128 + vw[cb]);
     } else {
       const u32x4 lo_ = __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[cb], d_k * 128, 0);
-      const u32x4 hi_ = __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[cb] + 64, d_k * 128, 0);
+      const u32x4 hi_ = __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[cb] + 16, d_k * 128, 0);
       w[cb] = make_frag_t<FP8>(lo_, hi_);
     }
   };
@@ -536,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       Tile t;
       t.rows = 0;
       while (np < hi_x) {
-        t = decode(table, NR, d_cur, np, ntn);
+        t = decode<16>(table, NR, d_cur, np, ntn);
         if (t.rows > 0) break;
         np += per_xcd;
       }
@@ -564,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
     Tile t;
     t.rows = 0;
     while (np < hi_x) {
-      t = decode(table, NR, c_cur, np, ntn);
+      t = decode<16>(table, NR, c_cur, np, ntn);
       if (t.rows > 0) break;
       np += per_xcd;
     }
@@ -685,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   // next step's first two fragments.
   bool c_epi = false, done = false;
   int c_nrb = __builtin_amdgcn_readfirstlane((ct.rows + 15) >> 4);
-  const int ck_lo = FP8 ? 2 * fg : fg, ck_hi = FP8 ? 2 * fg + 1 : fg + 4;
+  const int ck_lo = 2 * fg, ck_hi = 2 * fg + 1;
   const uint32_t a_lo = static_cast<uint32_t>(fr * 128 + ((ck_lo ^ swz(fr)) << 4));
   const uint32_t a_hi = static_cast<uint32_t>(fr * 128 + ((ck_hi ^ swz(fr)) << 4));
   // weight-scale dword of this wavefront's columns (plain: its 128-column block)

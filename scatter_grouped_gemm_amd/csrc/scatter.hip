@@ -36,19 +36,22 @@ struct ScatterWs {
   int32_t* total;   // [El] assignments of expert e
   int32_t* vstart;  // [El] assignments of the experts before e
   int32_t* src;     // [A] assignment t*k + j of valid row vstart[e] + rank
-  uint8_t* tscale;  // [T][H/128] FP8: each token's UE8M0 scale bytes
+  uint8_t* tscale;  // [T][tscale_ld(H)] FP8: each token's UE8M0 scale bytes
 };
 
 __host__ __device__ inline int64_t num_chunks(int64_t A) { return (A + kChunk - 1) / kChunk; }
 
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+// Row stride of the staged scale bytes: H/128 rounded up to whole 8-byte words.
+__host__ __device__ inline int tscale_ld(int H) { return (H / 128 + 7) & ~7; }
+
 // Scratch of a scatter of T tokens, top-k, El local experts, H channels.
 inline size_t ws_bytes(int64_t T, int k, int El, int H) {
   const int64_t A = T * k;
   return kWsHeader + align256(static_cast<size_t>(num_chunks(A)) * El * 4) +
          3 * align256(static_cast<size_t>(El) * 4) + align256(static_cast<size_t>(A) * 4) +
-         align256(static_cast<size_t>(T) * (H / 128));
+         align256(static_cast<size_t>(T) * tscale_ld(H));
 }
 
 inline ScatterWs carve(void* ws, int64_t T, int k, int El) {
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
         const uint32_t hi = e4m3x4(f[4], f[5], f[6], f[7], e);
         const uint2 q = make_uint2(lo, hi);
         if ((threadIdx.x & 15) == 0)
-          tscale[static_cast<int64_t>(t) * HB + col / 128] = static_cast<uint8_t>(e + 127);
+          tscale[static_cast<int64_t>(t) * tscale_ld(H) + col / 128] = static_cast<uint8_t>(e + 127);
         for (int j = 0; j < k; ++j) {
           const int r = rows[j];
           if (r < 0) continue;
@@ -470,8 +473,14 @@ __global__ __launch_bounds__(256) void scatter_scales_kernel(
       re = static_cast<int>(r - start[e]);
     }
     const int64_t t = src[vstart[e] + re] / k;
-    const uint8_t* ts = tscale + t * HB;
-    for (int b = 0; b < HB; ++b) scale_out[scale_index(r, b, rows, MASKED ? max_m : 0, HB)] = ts[b];
+    // the token's bytes as 8-byte words (rows of the staging array are whole
+    // words), then one byte per 128-channel block
+    const uint64_t* ts = reinterpret_cast<const uint64_t*>(tscale + t * ((HB + 7) & ~7));
+    for (int b0 = 0; b0 < HB; b0 += 8) {
+      const uint64_t v = ts[b0 >> 3];
+      for (int b = b0; b < b0 + 8 && b < HB; ++b)
+        scale_out[scale_index(r, b, rows, MASKED ? max_m : 0, HB)] = static_cast<uint8_t>(v >> (8 * (b - b0)));
+    }
   }
 }
 

@@ -60,9 +60,11 @@ def test_ws_bytes_grow_with_problem():
     b = L.moe_scatter_ws_bytes(16384, 8, 128, 256)
     c = L.moe_scatter_ws_bytes(16384, 8, 128, 7168)
     assert 0 < a < b < c
-    # at least the per-row assignment index (4 bytes per assignment) and one
-    # staged scale byte per token and 128 channels
-    assert c - b >= 16384 * (7168 - 256) // 128
+    # at least the per-row assignment index (4 bytes per assignment) and the
+    # staged scale bytes: one per token and 128 channels, each token's row
+    # rounded up to whole 8-byte words (56 bytes at H=7168, 8 at H=256)
+    assert c - b >= 16384 * (56 - 8)
+    assert c >= 16384 * 56 + 16384 * 8 * 4
     assert b >= 16384 * 8 * 4
     assert L.lib().moe_scatter_ws_bytes(-1, 2, 8, 256) == 0
     assert L.lib().moe_scatter_ws_bytes(4, 2, 8, -128) == 0

@@ -68,7 +68,7 @@ def test_memory_kernel_bytes_count_only_local_rows():
 def test_stored_traffic_is_reported_only_for_the_source_it_was_taken_on():
     assert bench.measured_traffic("no_such_workload", "w13") is None
     h = hashlib.sha256()
-    for src in ("gemm.hip", "gemm_wreg.hip", "gemm_wreg.h", "common.h"):
+    for src in ("gemm.hip", "gemm_wreg.hip", "gemm_wreg.h", "gemm_runs.h", "common.h"):
         with open(os.path.join(ROOT, "scatter_grouped_gemm_amd", "csrc", src), "rb") as f:
             h.update(f.read())
     assert bench.gemm_source_sha256() == h.hexdigest()
