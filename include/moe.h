@@ -84,13 +84,18 @@ int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_experts);
 /* Layout policy measured on MI355X in place of the rule above, which the pages
  * leave open ("Support DeepGEMM for standard MoE dispatch", comments section:
  * compact slower than masked up to a crossover in token count).  Timing the
- * whole path in both layouts over 16 .. 16384 tokens (DeepSeek-V3 and two BF16
- * shapes, 8 .. 256 local experts) put the masked layout 4-23% ahead up to 1024
- * tokens and within 2% of compact from 4096, where its E_local * T rows cost
- * far more memory.  Returns 1 (masked) when max_tokens <= 2048 and
- * max_tokens * num_local_experts <= 2^20 rows, else 0; -1 for a negative or
- * zero argument. */
-int32_t moe_choose_layout(int64_t max_tokens, int32_t num_local_experts);
+ * whole path in both layouts over 16 .. 16384 tokens (DeepSeek-V3 with 256 and
+ * 32 local experts, BF16 with 128 and 8) put the masked layout ahead while the
+ * experts hold few rows (up to about 64 per expert on average) and the
+ * compact layout level or ahead beyond, while the masked buffers grow as
+ * num_local_experts * max_tokens rows.  Returns 1 (masked) when
+ *   max_tokens * top_k <= 64 * num_experts            (mean rows per expert)
+ *   and num_local_experts * max_tokens <= 4 * moe_compact_rows_bound(
+ *       max_tokens * top_k, num_local_experts, block_e)   (memory cap),
+ * else 0 (compact); -1 for a zero or negative argument, more local experts
+ * than experts, or top_k above num_experts. */
+int32_t moe_choose_layout(int64_t max_tokens, int32_t top_k, int32_t num_experts,
+                          int32_t num_local_experts, int32_t block_e);
 
 /* Scratch bytes moe_scatter_compact / moe_scatter_masked need for T tokens,
  * top-k, num_local_experts local experts and H hidden channels (per-chunk

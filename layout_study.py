@@ -35,7 +35,7 @@ SHAPES = {
     "bf16_e128": (4096, 1536, 128, 128, 8, False, "bf16_skewed"),
     "bf16_e8": (4096, 14336, 8, 8, 2, False, "bf16_prefill"),
 }
-DEFAULT_TOKENS = [16, 64, 256, 1024, 4096, 8192, 16384]
+DEFAULT_TOKENS = [16, 64, 256, 1024, 1536, 2048, 3072, 4096, 8192, 16384]
 
 
 def log(*a):
@@ -87,7 +87,6 @@ def run_shape(name, tokens, steps, warmup, max_gib):
         for layout in ("compact", "masked"):
             gib = buffer_gib(layout, T, H, I, El, k, fp8)
             if gib > max_gib:
-                res[layout] = None
                 log(f"{name} T={T} {layout}: skipped ({gib:.1f} GiB of buffers)")
                 continue
             layer = make_layer(layout, T, H, I, E, El, k, fp8)
@@ -103,7 +102,7 @@ def run_shape(name, tokens, steps, warmup, max_gib):
             else:
                 layer.w13, layer.w13_scale, layer.w2, layer.w2_scale = weights
             ms, kern = time_layer(layer, x, logits, steps, warmup)
-            res[layout] = ms
+            res[layout] = dict(ms=ms, w13=kern.get("gemm_w13_silu"), gib=gib)
             line = dict(shape=name, T=T, H=H, I=I, E=E, E_local=El, k=k,
                         dtype="fp8_e4m3" if fp8 else "bf16", layout=layout,
                         ms_per_step=round(ms, 4), buffers_gib=round(gib, 2),
@@ -111,19 +110,47 @@ def run_shape(name, tokens, steps, warmup, max_gib):
             print(json.dumps(line), flush=True)
             del layer
             torch.cuda.empty_cache()
-        rows.append((T, res.get("compact"), res.get("masked")))
+        rows.append(dict(T=T, **{f"{lay}_{f}": v for lay, r in res.items() for f, v in r.items()}))
     return rows
 
 
 def markdown(results):
-    out = ["| shape | T | compact ms | masked ms | compact / masked |", "|---|---|---|---|---|"]
+    """Table of one sweep: whole-step and w13 times of both layouts, the masked
+    buffers' size, and the layout moe_choose_layout picks for the shape."""
+    from scatter_grouped_gemm_amd import _lib as L
+    out = ["| shape | T | compact ms | masked ms | compact / masked | compact w13 ms | masked w13 ms "
+           "| masked buffers GiB | compact buffers GiB | policy |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    f = lambda v, p=4: f"{v:.{p}f}" if v is not None else "-"
     for name, rows in results.items():
-        for T, c, m in rows:
-            fc = f"{c:.4f}" if c is not None else "skipped"
-            fm = f"{m:.4f}" if m is not None else "skipped"
-            r = f"{c / m:.3f}" if c is not None and m is not None else "-"
-            out.append(f"| {name} | {T} | {fc} | {fm} | {r} |")
+        H, I, E, El, k, fp8, _ = SHAPES[name]
+        for r in rows:
+            T = r["T"]
+            c, m = r.get("compact_ms"), r.get("masked_ms")
+            ratio = f"{c / m:.3f}" if c is not None and m is not None else "-"
+            pick = "masked" if L.moe_choose_layout(T, k, E, El) else "compact"
+            out.append(f"| {name} | {T} | {f(c)} | {f(m) if m is not None else 'skipped'} | {ratio} | "
+                       f"{f(r.get('compact_w13'), 3)} | {f(r.get('masked_w13'), 3)} | "
+                       f"{f(buffer_gib('masked', T, H, I, El, k, fp8), 2)} | "
+                       f"{f(buffer_gib('compact', T, H, I, El, k, fp8), 2)} | {pick} |")
     return "\n".join(out)
+
+
+def from_jsonl(path):
+    """Rebuild the per-shape rows of a sweep from the JSON lines it printed."""
+    results = {}
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            rows = results.setdefault(d["shape"], [])
+            if not rows or rows[-1]["T"] != d["T"]:
+                rows.append(dict(T=d["T"]))
+            lay = d["layout"]
+            rows[-1][f"{lay}_ms"] = d["ms_per_step"]
+            rows[-1][f"{lay}_w13"] = d["kernels_ms"].get("gemm_w13_silu")
+    return results
 
 
 def main(argv=None):
@@ -134,11 +161,16 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--max-gib", type=float, default=120.0)
     ap.add_argument("--md", default=None)
+    ap.add_argument("--from-jsonl", default=None,
+                    help="only rebuild the markdown table from the JSON lines of an earlier run")
     a = ap.parse_args(argv)
     tokens = [int(t) for t in a.tokens.split(",")]
-    results = {}
-    for name in a.shapes.split(","):
-        results[name] = run_shape(name, tokens, a.steps, a.warmup, a.max_gib)
+    if a.from_jsonl:
+        results = from_jsonl(a.from_jsonl)
+    else:
+        results = {}
+        for name in a.shapes.split(","):
+            results[name] = run_shape(name, tokens, a.steps, a.warmup, a.max_gib)
     md = markdown(results)
     print(md, file=sys.stderr, flush=True)
     if a.md:

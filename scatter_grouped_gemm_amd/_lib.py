@@ -27,7 +27,7 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 SIGNATURES = {
     "moe_compact_rows_bound": (_I64, [_I64, _I32, _I32]),
     "moe_use_masked_layout": (_I32, [_I32, _I32]),
-    "moe_choose_layout": (_I32, [_I64, _I32]),
+    "moe_choose_layout": (_I32, [_I64, _I32, _I32, _I32, _I32]),
     "moe_scatter_ws_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "moe_status_str": (ctypes.c_char_p, [_I32]),
     "moe_get_device_error": (_I32, [_P, _P, _P]),
@@ -125,10 +125,12 @@ def moe_use_masked_layout(num_experts: int, num_local_experts: int) -> bool:
     return bool(lib().moe_use_masked_layout(num_experts, num_local_experts))
 
 
-def moe_choose_layout(max_tokens: int, num_local_experts: int) -> bool:
-    r = lib().moe_choose_layout(max_tokens, num_local_experts)
+def moe_choose_layout(max_tokens: int, top_k: int, num_experts: int, num_local_experts: int,
+                      block_e: int = 128) -> bool:
+    r = lib().moe_choose_layout(max_tokens, top_k, num_experts, num_local_experts, block_e)
     if r < 0:
-        raise ValueError("moe_choose_layout: sizes must be positive")
+        raise ValueError("moe_choose_layout: sizes must be positive, num_local_experts <= num_experts "
+                         "and top_k <= num_experts")
     return bool(r)
 
 

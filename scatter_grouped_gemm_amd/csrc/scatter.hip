@@ -521,11 +521,21 @@ extern "C" int32_t moe_use_masked_layout(int32_t num_experts, int32_t num_local_
   return (num_experts > num_local_experts && num_local_experts <= 32) ? 1 : 0;
 }
 
-// Measured on MI355X: masked ahead up to ~1024 tokens, level from ~4096, where
-// its rows (one max_tokens slab per local expert) cost the most memory.
-extern "C" int32_t moe_choose_layout(int64_t max_tokens, int32_t num_local_experts) {
-  if (max_tokens <= 0 || num_local_experts <= 0) return -1;
-  return (max_tokens <= 2048 && max_tokens * num_local_experts <= (1ll << 20)) ? 1 : 0;
+// Measured on MI355X (whole expert path, both layouts, 16 .. 16384 tokens):
+// masked wins while experts hold few rows (its 16/32/64-row tiles), compact
+// from about 64 rows per expert on; masked buffers (E_local * max_tokens rows)
+// are capped at kMaskedRowsFactor times the compact bound.
+constexpr int64_t kMaskedMeanRows = 64;
+constexpr int64_t kMaskedRowsFactor = 4;
+extern "C" int32_t moe_choose_layout(int64_t max_tokens, int32_t top_k, int32_t num_experts,
+                                     int32_t num_local_experts, int32_t block_e) {
+  if (max_tokens <= 0 || top_k <= 0 || num_experts <= 0 || num_local_experts <= 0 ||
+      num_local_experts > num_experts || top_k > num_experts || block_e <= 0 || max_tokens > (1ll << 40))
+    return -1;
+  const int64_t compact = moe_compact_rows_bound(max_tokens * top_k, num_local_experts, block_e);
+  const bool few_rows = max_tokens * top_k <= kMaskedMeanRows * num_experts;
+  const bool fits = max_tokens * num_local_experts <= kMaskedRowsFactor * compact;
+  return (few_rows && fits) ? 1 : 0;
 }
 
 static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start, int32_t El,

@@ -7,8 +7,9 @@ construction from (max_tokens, k, num_local_experts, block_e), so a forward
 never reads device data back to the host and can be captured in a HIP graph.
 
 Layout choice: ``layout="auto"`` takes the policy measured on MI355X
-(moe_choose_layout: masked up to 2048 tokens per batch while its rows stay
-within 2^20, compact beyond); ``layout="rule"`` takes the rule of "Support
+(moe_choose_layout: masked while experts hold at most 64 rows on average and
+its buffers stay within 4x the compact bound, compact beyond); ``layout="rule"``
+takes the rule of "Support
 DeepGEMM for standard MoE dispatch", implementation breakdown item 2 (masked
 when there are non-local experts and at most 32 local ones).  The activation dtype
 follows the weights ("[Feature] Support BF16 and batch-invariant inference
@@ -46,7 +47,7 @@ class MoELayer:
         self.T_max = max_tokens
         self.device = torch.device(device)
         if layout == "auto":
-            layout = "masked" if L.moe_choose_layout(max_tokens, self.El) else "compact"
+            layout = "masked" if L.moe_choose_layout(max_tokens, top_k, self.E, self.El, block_e) else "compact"
         elif layout == "rule":
             layout = "masked" if L.moe_use_masked_layout(self.E, self.El) else "compact"
         if layout not in ("compact", "masked"):

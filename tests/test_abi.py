@@ -40,11 +40,24 @@ def test_host_helpers_match_oracle(orc):
         assert L.moe_compact_rows_bound(A, E, B) == orc.compact_rows_bound(A, E, B)
     for E, El in [(256, 32), (256, 33), (8, 8), (64, 1), (32, 32)]:
         assert L.moe_use_masked_layout(E, El) == orc.use_masked_layout(E, El)
-    # the measured layout policy: masked up to 2048 tokens within 2^20 rows
-    for T, El, want in [(1, 256, 1), (2048, 256, 1), (2049, 8, 0), (4096, 32, 0), (2048, 513, 0),
-                        (1024, 1024, 1), (1024, 1025, 0)]:
-        assert L.moe_choose_layout(T, El) == bool(want), (T, El)
-    assert L.lib().moe_choose_layout(0, 8) == -1 and L.lib().moe_choose_layout(8, 0) == -1
+    # the measured layout policy: masked while T*k <= 64*E and E_local*T <= 4x
+    # the compact bound; the cases are the measured shapes on both sides of
+    # their crossovers (T, k, E, E_local, masked?)
+    for T, k, E, El, want in [(256, 8, 256, 256, 1), (512, 8, 256, 256, 1), (1024, 8, 256, 256, 0),
+                              (1024, 8, 256, 32, 1), (2048, 8, 256, 32, 1), (3072, 8, 256, 32, 0),
+                              (256, 8, 128, 128, 1), (1024, 8, 128, 128, 0), (16, 8, 128, 128, 1),
+                              (256, 2, 8, 8, 1), (1024, 2, 8, 8, 0), (1, 1, 1, 1, 1)]:
+        assert L.moe_choose_layout(T, k, E, El) == bool(want), (T, k, E, El)
+    # whatever the shape, a masked pick never holds more than 4x the compact rows
+    for T in (1, 7, 64, 300, 1000, 2048, 5000, 20000):
+        for k, E, El in [(8, 256, 256), (8, 256, 32), (2, 8, 8), (8, 128, 128), (6, 64, 64), (8, 256, 8)]:
+            if L.moe_choose_layout(T, k, E, El):
+                assert El * T <= 4 * L.moe_compact_rows_bound(T * k, El, 128), (T, k, E, El)
+                assert T * k <= 64 * E
+    lib = L.lib()
+    for bad in [(0, 8, 256, 256, 128), (8, 0, 256, 256, 128), (8, 8, 0, 1, 128), (8, 8, 256, 0, 128),
+                (8, 8, 16, 32, 128), (8, 9, 8, 8, 128), (8, 8, 256, 256, 0)]:
+        assert lib.moe_choose_layout(*bad) == -1, bad
     assert L.lib().moe_compact_rows_bound(-1, 8, 128) == -1
     assert L.lib().moe_compact_rows_bound(10, 0, 128) == -1
 
