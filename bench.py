@@ -111,6 +111,7 @@ def gemm_work(wl, layer, torch):
     rows2 = L.grouped_gemm_rows_executed(layer.wdt, masked, c, layer.expected_m, M, H, I)
     return dict(assignments=A, active_experts=active, w13_flops=w13_flops, w2_flops=w2_flops,
                 exec_flops=2.0 * (rows13 * 2 * I * H + rows2 * H * I),
+                w13_exec_flops=2.0 * rows13 * 2 * I * H, w2_exec_flops=2.0 * rows2 * H * I,
                 w13_bytes=w13_bytes, w2_bytes=w2_bytes)
 
 
@@ -487,6 +488,8 @@ def main():
         "gemm": {"tflops_both": round(gemm_tflops, 1),
                  "executed_tflops_both": round(work["exec_flops"] / (gemm_ms * 1e-3) / 1e12, 1),
                  "mfma_frac_both": round(gemm_tflops / PEAK_TFLOPS[dtype], 4),
+                 "flops": {"w13": work["w13_flops"], "w2": work["w2_flops"]},
+                 "executed_flops": {"w13": work["w13_exec_flops"], "w2": work["w2_exec_flops"]},
                  "w2": w2_roof},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "memory_kernels": memory_kernels(wl, layer, kern, work),

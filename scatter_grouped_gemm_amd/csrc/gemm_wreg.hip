@@ -30,8 +30,13 @@
 //     block scale are constant over one k-step) or two v_mfma_f32_16x16x32_bf16.
 //     The weight fragment is the MFMA "A" operand, so each lane ends with four
 //     consecutive output columns of one row; the weight rows a lane loads are
-//     permuted so that two column blocks give eight consecutive columns, one
-//     16-byte store (bf16) per lane and row block pair.
+//     permuted so that two column blocks give eight consecutive columns (16
+//     bytes of bf16).  The plain (w2) epilogue passes them through the stage
+//     just consumed, 64 rows at a time, and stores whole 128-byte row segments
+//     (8 rows per instruction): stores of 16 rows x 64 bytes cost the texture
+//     unit several times more per byte, and staging took the FP8 w2 of the
+//     DeepSeek-V3 prefill from 1.29 to 1.25 ms (the SiLU epilogues staged the
+//     same way measured no faster, FP8 slower, and store directly).
 //   - The k loop is one flat stream of k-steps over all of the workgroup's
 //     tiles: loads cross into the next tile while the current one finishes.
 //     Each step waits for its own loads with one vmcnt count (vector memory
@@ -391,22 +396,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
   // Stores of the finished tile ct, then zero accumulators.  The stores are
   // buffer stores bounded by the tile's rows (rows past the tile fall outside
   // the buffer and are dropped), so no lane-dependent branch guards them.
-  auto epilogue = [&]() __attribute__((always_inline)) {
+  // stg is the LDS stage of the tile's last k-step: every wavefront has read
+  // its fragments once all have reached the epilogue, and its next refill is
+  // issued only after the next step's barrier.
+  auto epilogue = [&](uint8_t* const stg) __attribute__((always_inline)) {
     if constexpr (EPI == kWrEpiPlain) {
       const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<uint16_t*>(p.C) + ct.row * p.N, 0, static_cast<int>(ct.rows * p.N * 2), 0x00020000);
-      const uint32_t c0 = static_cast<uint32_t>((fr * p.N + ct.nt * 256 + wave * 64 + fg * 8) * 2);
+      // through LDS, 64 rows at a time: each wavefront writes its 64 x 64
+      // block into its own 8 KB of the stage just consumed, then stores it as
+      // 8 rows x 128 bytes per instruction
+      __builtin_amdgcn_s_barrier();  // every wavefront is done reading the stage
+      uint8_t* const reg = stg + wave * 8192;
+      const int lr8 = lane >> 3;
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        f32x4 av[4];
-        acc_read(acc[rb], av);
+      for (int ps = 0; ps < 4; ++ps) {
+        if (ps * 64 >= ct.rows) break;
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const f32x4 a = av[2 * pr], b = av[2 * pr + 1];
-          const u32x4 v{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                        pack_bf16x2(b[2], b[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rc, c0 + static_cast<uint32_t>(rb * 16 * p.N * 2 + pr * 64),
-                                                 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          f32x4 av[4];
+          acc_read(acc[ps * 4 + q], av);
+          const int r = q * 16 + fr;
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const f32x4 a = av[2 * pr], b = av[2 * pr + 1];
+            const u32x4 v{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                          pack_bf16x2(b[2], b[3])};
+            *reinterpret_cast<u32x4*>(reg + r * 128 + (((pr * 4 + fg) ^ (r & 7)) << 4)) = v;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = j * 8 + lr8;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, rc, static_cast<uint32_t>(((ps * 64 + r) * p.N + ct.nt * 256 + wave * 64) * 2 + (lane & 7) * 16),
+              0, 0);
         }
       }
     } else {
@@ -568,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wreg_kernel(const WregArgs p
       mfma_drain();
       // the accumulator copies of the epilogue stay after the drain
       __builtin_amdgcn_sched_barrier(0);
-      epilogue();
+      epilogue(const_cast<uint8_t*>(S));
       done = cn.rows <= 0;
       ct = cn;
       c_nrb = __builtin_amdgcn_readfirstlane((ct.rows + 15) >> 4);
