@@ -27,7 +27,7 @@
 namespace moe {
 
 constexpr int kChunk = 256;    // assignments per wavefront chunk
-constexpr int kWsHeader = 256;  // bytes: device error word + padding
+constexpr int kWsHeader = 256;  // bytes: device error word, the scan's ticket, padding
 
 struct ScatterWs {
   int32_t* err;
@@ -83,7 +83,10 @@ __global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __res
   const int c = blockIdx.x * 4 + w;
   int* cnt = lds_i + w * El;
   for (int e = lane; e < El; e += 64) cnt[e] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    err[0] = 0;
+    err[1] = 0;  // the scan's ticket
+  }
   __syncthreads();
   if (c < C) {
     const int64_t a0 = static_cast<int64_t>(c) * kChunk;
@@ -98,31 +101,30 @@ __global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __res
     for (int e = lane; e < El; e += 64) counts[static_cast<int64_t>(c) * El + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads.  The chunk counts of expert e are split
-// into G = 1024 / El contiguous groups of chunks; thread (g, e) sums group g
-// (all of its loads in flight together), the group sums give each group's
-// base, and a second pass over the group writes the exclusive per-chunk
-// offsets in place.  Threads e < El then scan the padded expert sizes (wave
-// shuffles, then the wave totals).  El <= 1024.
-__global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict__ counts, int C,
-                                                            int El, int block_e, int clamp,
-                                                            int32_t* __restrict__ start,
-                                                            int32_t* __restrict__ total,
-                                                            int32_t* __restrict__ vstart,
-                                                            int32_t* __restrict__ start_out,
-                                                            int32_t* __restrict__ valid_out) {
-  __shared__ int part[1024];
-  __shared__ int64_t wsum[16];
-  __shared__ int64_t wsum_v[16];
+// Step 2, over ceil(El / 4) workgroups: wavefront e takes expert e's chunk
+// counts (lane l a contiguous run of ceil(C / 64) chunks, loads batched),
+// writes the exclusive per-chunk offsets in place and the expert's total.
+// The last workgroup to finish (a ticket in the workspace header, zeroed by
+// the count kernel; release by a fence before the ticket, acquire by a fence
+// after it) scans the padded and the plain sizes over the experts.
+__global__ __launch_bounds__(256) void scatter_scan_kernel(int32_t* __restrict__ counts, int C,
+                                                           int El, int block_e, int clamp,
+                                                           int32_t* __restrict__ start,
+                                                           int32_t* __restrict__ total,
+                                                           int32_t* __restrict__ vstart,
+                                                           int32_t* __restrict__ start_out,
+                                                           int32_t* __restrict__ valid_out,
+                                                           int32_t* __restrict__ ticket) {
+  __shared__ int64_t wsum[4];
+  __shared__ int64_t wsum_v[4];
+  __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int G = 1024 / El;
-  const int e = tid % El, g = tid / El;
-  const bool act = g < G;
-  const int cpg = (C + G - 1) / G;
-  const int c0 = g * cpg, c1 = c0 + cpg < C ? c0 + cpg : C;
-  constexpr int B = 16;
-  int sum = 0;
-  if (act) {
+  const int e = blockIdx.x * 4 + w;
+  if (e < El) {
+    const int per = (C + 63) / 64;
+    const int c0 = min(lane * per, C), c1 = min(c0 + per, C);
+    constexpr int B = 8;
+    int sum = 0;
     for (int cb = c0; cb < c1; cb += B) {
       int v[B];
 #pragma unroll
@@ -130,17 +132,14 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
 #pragma unroll
       for (int j = 0; j < B; ++j) sum += v[j];
     }
-    part[tid] = sum;
-  }
-  __syncthreads();
-  int run = 0;  // expert e's local assignments
-  if (act) {
-    int base = 0;
-    for (int q = 0; q < G; ++q) {
-      const int v = part[q * El + e];
-      if (q < g) base += v;
-      run += v;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
     }
+    int base = incl - sum;
+    const int tot = __shfl(incl, 63, 64);
     for (int cb = c0; cb < c1; cb += B) {
       int v[B];
 #pragma unroll
@@ -151,12 +150,29 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
         base += v[j];
       }
     }
+    if (lane == 0) total[e] = tot;
   }
-  // exclusive scans of the padded and the plain sizes over the experts
-  // (threads tid < El)
-  const int64_t padded = tid < El ? static_cast<int64_t>(run + block_e - 1) / block_e * block_e : 0;
-  const int64_t plain = tid < El ? run : 0;
-  int64_t incl = padded, incl_v = plain;
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // thread t takes experts 4t .. 4t + 3 (El <= 1024)
+  int run[4];
+  int64_t pad[4];
+  int64_t sp = 0, sv = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ee = tid * 4 + j;
+    run[j] = ee < El ? total[ee] : 0;
+    pad[j] = static_cast<int64_t>(run[j] + block_e - 1) / block_e * block_e;
+    sp += pad[j];
+    sv += run[j];
+  }
+  int64_t incl = sp, incl_v = sv;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int64_t v = __shfl_up(incl, off, 64);
@@ -175,13 +191,18 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int32_t* __restrict_
     incl += wsum[q];
     incl_v += wsum_v[q];
   }
-  if (tid < El) {
-    const int32_t st = static_cast<int32_t>(incl - padded);
-    start[tid] = st;
-    total[tid] = run;
-    vstart[tid] = static_cast<int32_t>(incl_v - plain);
-    if (start_out) start_out[tid] = st;
-    if (valid_out) valid_out[tid] = static_cast<int32_t>(clamp > 0 && run > clamp ? clamp : run);
+  int64_t bp = incl - sp, bv = incl_v - sv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ee = tid * 4 + j;
+    if (ee < El) {
+      start[ee] = static_cast<int32_t>(bp);
+      vstart[ee] = static_cast<int32_t>(bv);
+      if (start_out) start_out[ee] = static_cast<int32_t>(bp);
+      if (valid_out) valid_out[ee] = static_cast<int32_t>(clamp > 0 && run[j] > clamp ? clamp : run[j]);
+    }
+    bp += pad[j];
+    bv += run[j];
   }
 }
 
@@ -452,14 +473,25 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
 // (consecutive threads write consecutive bytes of each 128-channel block's
 // scale line): valid row r of expert e has rank r_e inside e; its token is
 // src[vstart[e] + r_e] / k, whose staged bytes are copied.  Compact rows take
-// e from m_indices (padding rows are skipped); masked row r belongs to group
+// Compact: the expert of row r is found as fill_m_indices_kernel finds it,
+// and m_indices[r] is written here too (the FP8 path has no separate fill
+// launch); padding rows get -1 and no scales.  Masked row r belongs to group
 // r / max_m and is valid below min(total, max_m).
 template <bool MASKED>
 __global__ __launch_bounds__(256) void scatter_scales_kernel(
-    const int32_t* __restrict__ m_indices, const int32_t* __restrict__ start,
+    int32_t* __restrict__ m_indices, const int32_t* __restrict__ start,
     const int32_t* __restrict__ total, const int32_t* __restrict__ vstart,
     const int32_t* __restrict__ src, const uint8_t* __restrict__ tscale, int k, int HB,
-    int64_t rows, int max_m, uint8_t* __restrict__ scale_out) {
+    int64_t rows, int max_m, int El, uint8_t* __restrict__ scale_out) {
+  __shared__ int s_start[MASKED ? 1 : 1024];
+  __shared__ int s_total[MASKED ? 1 : 1024];
+  if (!MASKED) {
+    for (int e = threadIdx.x; e < El; e += blockDim.x) {
+      s_start[e] = start[e];
+      s_total[e] = total[e];
+    }
+    __syncthreads();
+  }
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < rows;
        r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     int e, re;
@@ -468,9 +500,16 @@ __global__ __launch_bounds__(256) void scatter_scales_kernel(
       re = static_cast<int>(r - static_cast<int64_t>(e) * max_m);
       if (re >= min(total[e], max_m)) continue;
     } else {
-      e = m_indices[r];
-      if (e < 0) continue;
-      re = static_cast<int>(r - start[e]);
+      int lo = 0, hi = El - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_start[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      const bool valid = r - s_start[lo] < s_total[lo];
+      m_indices[r] = valid ? lo : -1;
+      if (!valid) continue;
+      e = lo;
+      re = static_cast<int>(r - s_start[lo]);
     }
     const int64_t t = src[vstart[e] + re] / k;
     // the token's bytes as 8-byte words (rows of the staging array are whole
@@ -573,8 +612,9 @@ static int32_t launch_front(const int32_t* ids, int64_t A, int32_t expert_start,
     scatter_count_kernel<<<1, 256, lds, s>>>(ids, 0, expert_start, El, 0, w.counts, w.err);
   }
   MOE_CHECK_LAUNCH();
-  scatter_scan_kernel<<<1, 1024, 0, s>>>(w.counts, C, El, masked ? 1 : block_e, masked ? max_m : 0,
-                                         w.start, w.total, w.vstart, start_out, valid_out);
+  scatter_scan_kernel<<<(El + 3) / 4, 256, 0, s>>>(w.counts, C, El, masked ? 1 : block_e,
+                                                  masked ? max_m : 0, w.start, w.total, w.vstart,
+                                                  start_out, valid_out, w.err + 1);
   MOE_CHECK_LAUNCH();
   if (C > 0) {
     if (masked)
@@ -603,7 +643,9 @@ static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const i
   int32_t st = launch_front(topk_ids, A, expert_start, El, block_e, w, expert_start_loc, num_valid, false, 0,
                     src2dst, s);
   if (st != MOE_OK) return st;
-  if (rows_capacity > 0) {
+  const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
+  // the FP8 scale pass writes m_indices itself
+  if (rows_capacity > 0 && !(fp8 && T > 0)) {
     int64_t nb = (rows_capacity + 255) / 256;
     if (nb > 2048) nb = 2048;
     fill_m_indices_kernel<<<static_cast<int>(nb), 256, 0, s>>>(w.start, w.total, El, rows_capacity,
@@ -611,7 +653,6 @@ static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const i
     MOE_CHECK_LAUNCH();
   }
   if (T > 0) {
-    const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3_UE8M0;
     if (fp8)
       scatter_rows_kernel<true><<<T, 256, 0, s>>>(static_cast<const uint16_t*>(x), H, k, src2dst,
                                                   static_cast<uint8_t*>(x_out), w.tscale);
@@ -622,7 +663,7 @@ static int32_t scatter_compact_body(const void* x, int32_t T, int32_t H, const i
     if (fp8 && rows_capacity > 0) {
       const int64_t nb = std::min<int64_t>((rows_capacity + 255) / 256, 2048);
       scatter_scales_kernel<false><<<static_cast<int>(nb), 256, 0, s>>>(
-          m_indices, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows_capacity, 0,
+          m_indices, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows_capacity, 0, El,
           scale_out);
       MOE_CHECK_LAUNCH();
     }
@@ -738,7 +779,7 @@ extern "C" int32_t moe_scatter_masked(const void* x, int32_t T, int32_t H, const
       const int64_t rows = static_cast<int64_t>(El) * max_m;
       const int64_t nb = std::min<int64_t>((rows + 255) / 256, 2048);
       scatter_scales_kernel<true><<<static_cast<int>(nb), 256, 0, s>>>(
-          nullptr, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows, max_m, scale_out);
+          nullptr, w.start, w.total, w.vstart, w.src, w.tscale, k, H / 128, rows, max_m, El, scale_out);
       MOE_CHECK_LAUNCH();
     }
   }
