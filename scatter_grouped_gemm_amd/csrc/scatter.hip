@@ -124,13 +124,18 @@ __global__ __launch_bounds__(256) void scatter_scan_kernel(int32_t* __restrict__
     const int per = (C + 63) / 64;
     const int c0 = min(lane * per, C), c1 = min(c0 + per, C);
     constexpr int B = 8;
+    // runs of up to B chunks (C <= 512) stay in registers between the passes
+    int keep[B] = {};
     int sum = 0;
     for (int cb = c0; cb < c1; cb += B) {
       int v[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? counts[static_cast<int64_t>(cb + j) * El + e] : 0;
 #pragma unroll
-      for (int j = 0; j < B; ++j) sum += v[j];
+      for (int j = 0; j < B; ++j) {
+        sum += v[j];
+        keep[j] = v[j];
+      }
     }
     int incl = sum;
 #pragma unroll
@@ -140,14 +145,22 @@ __global__ __launch_bounds__(256) void scatter_scan_kernel(int32_t* __restrict__
     }
     int base = incl - sum;
     const int tot = __shfl(incl, 63, 64);
-    for (int cb = c0; cb < c1; cb += B) {
-      int v[B];
-#pragma unroll
-      for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? counts[static_cast<int64_t>(cb + j) * El + e] : 0;
+    if (per <= B) {
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        if (cb + j < c1) counts[static_cast<int64_t>(cb + j) * El + e] = base;
-        base += v[j];
+        if (c0 + j < c1) counts[static_cast<int64_t>(c0 + j) * El + e] = base;
+        base += keep[j];
+      }
+    } else {
+      for (int cb = c0; cb < c1; cb += B) {
+        int v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? counts[static_cast<int64_t>(cb + j) * El + e] : 0;
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+          if (cb + j < c1) counts[static_cast<int64_t>(cb + j) * El + e] = base;
+          base += v[j];
+        }
       }
     }
     if (lane == 0) total[e] = tot;
