@@ -57,12 +57,17 @@ SCATTER_CASES = [
     (2000, 128, 128, 128, 0, 8, False),
     (1500, 7168, 256, 256, 0, 8, True),
     (257, 4096, 128, 128, 0, 8, False),
-    # more than 16384 assignments: the chunked count / scan / rank kernels,
-    # with the scan's chunk groups per expert uneven (20 chunks over 3
-    # groups), one group per expert, and more groups than chunks
+    # more than 16384 assignments: the chunked count / scan / rank kernels.
+    # The scan runs one wavefront per expert over ceil(El / 4) workgroups, the
+    # last of them scanning the expert sizes: El not a multiple of 4, the
+    # 1024-expert maximum (256 workgroups), a single workgroup, uneven chunk
+    # runs per lane, and more than 512 chunks (runs longer than the 8 kept in
+    # registers take a second pass)
     (2500, 128, 300, 300, 0, 8, True),
     (4100, 256, 1000, 700, 300, 4, False),
     (6000, 128, 3, 3, 0, 3, False),
+    (2200, 128, 1024, 1024, 0, 8, False),
+    (20000, 128, 64, 16, 8, 8, True),
 ]
 
 
