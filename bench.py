@@ -427,8 +427,8 @@ def cpu_baseline(wl, x, logits, target_s, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the expert path on a single MI355X "
-              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the expert path here runs one GPU's share of the "
+              f"experts on a single MI355X (--gpus {args.gpus} is not supported).", file=sys.stderr)
         sys.exit(2)
     import torch
 
