@@ -257,8 +257,9 @@ def workload_summary(wl, layer, ms, kern, torch):
     return out
 
 
-def other_workloads(names, torch, steps, warmup=3):
-    """The further seeded workloads, each built, timed and freed in turn."""
+def other_workloads(names, torch, steps, warmup=3, cpu=True):
+    """The further seeded workloads, each built, timed and freed in turn (with
+    the oracle's per-stage host timing unless cpu is False)."""
     from scatter_grouped_gemm_amd import inputs
     out = {}
     for name in names:
@@ -268,6 +269,9 @@ def other_workloads(names, torch, steps, warmup=3):
         ms, kern = time_steps(layer, x, logits, steps, warmup, torch)
         log(f"{name}: {ms:.3f} ms/step; " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
         out[name] = workload_summary(wl, layer, ms, kern, torch)
+        if cpu:
+            n_tok, reps = CPU_STAGE_TOKENS.get(wl.name, (min(wl.T, 64), 1))
+            out[name]["cpu_stages"] = cpu_stages(wl, x, logits, min(n_tok, wl.T), reps)
         del layer, x, logits
         torch.cuda.empty_cache()
     return out
@@ -424,6 +428,90 @@ def cpu_baseline(wl, x, logits, target_s, torch):
                        f"({n_exp} experts), {dt:.1f}s on {cores} threads")
 
 
+def cpu_stages(wl, x, logits, n_tok, reps=1):
+    """The oracle's layout path stage by stage on the first n_tok tokens of the
+    batch (route -> scatter -> w13 -> SiLU-mul (+ requant) -> w2 -> combine),
+    each stage timed with perf_counter on the host cores; the median over
+    `reps` runs.  The sample's experts are renumbered densely (experts without
+    tokens in the sample are left out of the layout); weight preparation is not
+    timed."""
+    import numpy as np
+
+    import oracle
+    from scatter_grouped_gemm_amd import inputs
+    oracle.build(force=False)
+    xs = inputs.bf16_bits(x[:n_tok])
+    ls = logits[:n_tok].cpu().numpy()
+    ids, tw = oracle.route_topk(ls, wl.k)
+    local = ids - wl.expert_start
+    inside = (local >= 0) & (local < wl.El)
+    need = sorted({int(e) for e in local[inside].reshape(-1)})
+    remap = np.full(wl.El, -1, np.int32)
+    remap[need] = np.arange(len(need), dtype=np.int32)
+    ids_c = np.where(inside, remap[np.clip(local, 0, wl.El - 1)], -1).astype(np.int32)
+    w13, w2 = [], []
+    for e in need:
+        a, b = inputs.expert_weights(wl, wl.expert_start + e, x.device)
+        w13.append(inputs.bf16_bits(a)[None])
+        w2.append(inputs.bf16_bits(b)[None])
+    w13, w2 = np.concatenate(w13), np.concatenate(w2)
+    if wl.fp8:
+        w13, w2 = oracle.quant_weight_blocks(w13), oracle.quant_weight_blocks(w2)
+    El = len(need)
+    masked = wl.layout == "masked"
+    names = ("route", "scatter", "w13", "silu_mul", "w2", "combine")
+    runs = []
+    for _ in range(reps):
+        t = [time.perf_counter()]
+        ids2, tw2 = oracle.route_topk(ls, wl.k)
+        t.append(time.perf_counter())
+        if masked:
+            max_m = wl.max_m or n_tok
+            sc = oracle.scatter_masked(xs, ids_c, 0, El, max_m, wl.fp8)
+            rg = oracle.masked_row_group(sc["masked_m"], max_m)
+        else:
+            rows = oracle.compact_rows_bound(n_tok * wl.k, El, wl.block_e)
+            sc = oracle.scatter_compact(xs, ids_c, 0, El, wl.block_e, rows, wl.fp8)
+            rg = sc["m_indices"]
+        t.append(time.perf_counter())
+        if wl.fp8:
+            h1 = oracle.gemm_fp8_rows(sc["x_out"], sc["scale_out"], w13[0], w13[1], rg)
+        else:
+            h1 = oracle.gemm_bf16_rows(sc["x_out"], w13, rg)
+        t.append(time.perf_counter())
+        act = oracle.silu_and_mul(h1, rg)
+        if wl.fp8:
+            aq = np.zeros(act.shape, np.uint8)
+            asc = np.zeros((act.shape[0], act.shape[1] // 128), np.uint8)
+            valid = rg >= 0
+            if valid.any():
+                aq[valid], asc[valid] = oracle.quant_rows(act[valid])
+        t.append(time.perf_counter())
+        if wl.fp8:
+            y = oracle.gemm_fp8_rows(aq, asc, w2[0], w2[1], rg)
+        else:
+            y = oracle.gemm_bf16_rows(act, w2, rg)
+        t.append(time.perf_counter())
+        out = oracle.combine(y, sc["src2dst"], tw2)
+        t.append(time.perf_counter())
+        assert np.array_equal(ids2, ids) and out.shape == (n_tok, wl.H)
+        runs.append([t[i + 1] - t[i] for i in range(len(names))])
+    med = np.median(np.asarray(runs), axis=0)
+    res = {f"{n}_s": round(float(v), 5) for n, v in zip(names, med)}
+    res.update(tokens=n_tok, experts=El, reps=reps, total_s=round(float(med.sum()), 5),
+               tokens_per_s=round(n_tok / float(med.sum()), 2))
+    log(f"oracle stages on {n_tok} tokens ({wl.name}): " + ", ".join(f"{n} {v:.3f}s" for n, v in zip(names, med)))
+    return res
+
+
+# tokens of each workload the oracle's stage timing runs on (whole batch and
+# median of 3 for the small ones; a few seconds of host time for the others)
+CPU_STAGE_TOKENS = {"tiny_bf16_T64_E8": (64, 3), "fp8_masked_decode_T256_E32of256": (256, 3),
+                    "fp8_prefill_T8192_H7168_I2048_E256": (256, 1),
+                    "bf16_prefill_T4096_H4096_I14336_E8": (128, 1),
+                    "bf16_skewed_T16384_H4096_I1536_E128": (256, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -509,11 +597,14 @@ def main():
             if isinstance(v, dict)))
     if not args.no_cpu_baseline and not layer.mx:
         res["cpu_baseline"] = cpu_baseline(wl, x, logits, args.cpu_seconds, torch)
+        n_tok, reps = CPU_STAGE_TOKENS.get(wl.name, (min(wl.T, 64), 1))
+        res["cpu_baseline"]["stages"] = cpu_stages(wl, x, logits, min(n_tok, wl.T), reps)
     names = [n for n in args.workloads.split(",") if n and n != args.workload]
     if names:
         del layer, x, logits
         torch.cuda.empty_cache()
-        res["workloads"] = other_workloads(names, torch, args.workload_steps)
+        res["workloads"] = other_workloads(names, torch, args.workload_steps,
+                                           cpu=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
