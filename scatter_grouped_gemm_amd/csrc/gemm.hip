@@ -1,6 +1,11 @@
 // Grouped NT GEMM for the expert layouts: C[r, :] = A[r, :] . B[g(r)]^T,
 // BF16 or FP8 e4m3 with UE8M0 scales, fp32 accumulation, bf16 output.
 //
+// The compact-layout calls with BF16 or 128x128-block FP8 weights and N a
+// multiple of 256 go to the register-streamed kernel (gemm_wreg.hip); the
+// kernel here serves the masked layout, the MX weight formats and the other
+// shapes, and holds the entry points and their argument checks for both.
+//
 // Design (gfx950, wave64, 160 KB LDS):
 //   - Persistent workgroups of 512 threads (8 wavefronts, two per SIMD), one
 //     per CU.  A tile of C is BM x BN (128 x 256; 128 x 128 when N % 256 != 0;
