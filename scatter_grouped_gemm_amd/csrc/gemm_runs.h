@@ -1,7 +1,7 @@
-// Tile order of the compact-layout grouped GEMMs, shared by the kernels in
-// gemm_wreg.hip and gemm_lds.hip: the run table each workgroup builds from
-// m_indices, the position -> tile decoder, and the small LDS and wait helpers
-// the kernels use around it.
+// Tile order of the compact-layout register-streamed grouped GEMM
+// (gemm_wreg.hip): the run table each workgroup builds from m_indices, the
+// position -> tile decoder, and the small LDS and wait helpers the kernel uses
+// around it.
 //
 // Order: expert runs (maximal stretches of 128-row blocks with one expert id)
 // in row order; a run of z valid rows is cut into ceil(z / 256) M-tiles of
