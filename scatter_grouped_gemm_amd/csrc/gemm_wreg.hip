@@ -5,14 +5,15 @@
 //
 // Why this shape (gfx950, one MI355X):
 //   - In the FP8 DeepSeek-V3-shaped prefill each expert holds about 256 token
-//     rows against a 4096 x 7168 weight matrix, so the weights are read about
-//     once per 256 rows and the GEMMs are bound by how fast the weight bytes
-//     arrive, not by the MFMAs.  What limits the arrival rate per CU is the
-//     bytes it keeps in flight.  Staging the weights through LDS caps that at a
-//     few 48 KB stages; here every wavefront loads its own weight columns
-//     straight into VGPRs in MFMA fragment order (buffer_load_dwordx4), four
-//     k-steps ahead, so a CU keeps 128 KB of weights plus four 32 KB
-//     activation stages in flight.
+//     rows against a 4096 x 7168 weight matrix, so every k-step a CU moves 64
+//     KB (256 activation rows and 256 weight rows, 128 bytes each) for at most
+//     256 x 256 x 128 multiply-adds.  Measured, a step is bound by issuing
+//     those loads (about 72 vector memory instructions per CU) and by how
+//     little that overlaps the MFMAs of the same wavefront, not by latency:
+//     the per-step wait for data is short.  Every wavefront loads its own
+//     weight columns straight into VGPRs in MFMA fragment order (16 bytes per
+//     lane), three k-steps ahead in four register sets, so the weights never
+//     pass through LDS; the activations go through four 32 KB LDS stages.
 //   - Workgroup = 4 wavefronts (one per SIMD, 512 registers each).  A tile is
 //     up to 256 rows of one expert run by 256 weight columns; wavefront w owns
 //     64 columns and all rows, so the activations (shared by every wavefront)
@@ -42,7 +43,7 @@
 //     Each step waits for its own loads with one vmcnt count (vector memory
 //     instructions complete in issue order; every step issues the same
 //     number), one barrier makes the activation stage visible, and the stage
-//     and register set of the step before are refilled with the step four
+//     and register set of the step before are refilled with the step three
 //     ahead.
 //   - Tile order (built once per workgroup from m_indices): expert runs in
 //     row order; inside a run, groups of up to 8 M-tiles, N-tiles in order,
